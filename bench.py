@@ -1,0 +1,227 @@
+"""Benchmark: microseconds per MoE layer-step of the expert-slot decode path on one MI355X.
+
+Workload (default): the GLM-shaped MoE layer -- H 6144, I 2048, 256 experts,
+top-8, 128 HBM slots, M=1 decode rows, NVFP4 weights, Zipf(1.1)-skewed routing
+with AR(1) drift -- for `--steps` timed steps after `--warmup` untimed ones.
+A step is one moe_layer_decode call: routing + remap/LRU, miss fills from the
+pinned host store, gate/up and down FP4 GEMVs, combine.  Inputs are resident in
+HBM before the timed region.  Between steps a 512 MiB buffer is rewritten so
+that the 256 MiB Infinity Cache cannot serve slot bytes from the previous step
+(in a real stack 74 other layers run in between); the per-step time is taken
+between HIP events recorded around the step's own kernels, so the flush is not
+counted.  Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per MoE layer-step (M=1) + achieved HBM GB/s vs peak; LRU hit rate"
+HBM_PEAK_GBS = 8000.0
+PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16, per direction
+PHASES = ("route_remap", "fill", "gateup", "down", "combine")
+KERNEL_NAMES = {"gateup": "k_gemv<6144, 1, true>", "down": "k_gemv<2048, 1, false>"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--config", default="glm")
+    ap.add_argument("--no-flush", action="store_true", help="back-to-back steps (Infinity Cache may serve repeats)")
+    ap.add_argument("--cpu-baseline-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def pmc_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_%s.json" % kernel_key)
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_sha256") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("expert_gemv.hip", "internal.h"):
+        h.update(open(os.path.join(ROOT, "hbm_expert_slot_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(cfg, logits, x_rows, start, nsteps):
+    """The oracle, as it stands, on `nsteps` steps of the same trace (bounded sample)."""
+    from oracle import OracleLayer, route
+    from synth import expert_blob, global_scales
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    # input generation (blob bytes) is not oracle work: stage them first
+    need = set()
+    for t in range(start, start + nsteps):
+        ids, _ = route(logits[t, :1], cfg.top_k)
+        need |= set(int(e) for e in ids.reshape(-1))
+    blobs = {e: expert_blob(cfg, 0, e) for e in sorted(need)}
+    gs = global_scales(cfg, 0, "unit")
+    orc = OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.slots, lambda e: blobs[e], gs,
+                      keep_slot_bytes=False)
+    t0 = time.perf_counter()
+    for t in range(start, start + nsteps):
+        orc.decode(logits[t, :1], x_rows[t])
+    dt = time.perf_counter() - t0
+    # bookkeeping alone (routing + slot bookkeeping) over the whole trace
+    from oracle.lru import SlotState
+    st = SlotState(cfg.n_experts, cfg.slots, cfg.top_k)
+    t1 = time.perf_counter()
+    for t in range(logits.shape[0]):
+        ids, _ = route(logits[t, :1], cfg.top_k)
+        st.step(ids)
+    bk = (time.perf_counter() - t1) / logits.shape[0]
+    return {
+        "value": dt / nsteps * 1e6, "unit": "us/layer-step", "cores": int(threads), "kind": "oracle",
+        "sample": "%d consecutive M=1 steps of the same GLM trace (full fp64 step: routing, LRU, dequant, "
+                  "expert math); blob generation excluded" % nsteps,
+        "bookkeeping_us_per_step": bk * 1e6,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: this build runs the path on a single MI355X "
+              "(no collectives); --gpus %d is not supported" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hbm_expert_slot_amd.cache import SlotCache
+    from synth import CONFIGS, activations, expert_blobs, global_scales, routing_trace
+
+    cfg = CONFIGS[a.config]
+    if cfg.rows != 1 or cfg.n_layers != 1:
+        print("bench.py times the single-layer M=1 workloads (tiny, glm)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    W, K = a.warmup, a.steps
+    T = W + K
+    print("bench: %s, %d warmup + %d timed steps" % (cfg.description, W, K), file=sys.stderr, flush=True)
+    sc = SlotCache(1, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.slots, 1)
+    t0 = time.time()
+    expert_blobs(cfg, 0, out=sc.backing(0))
+    sc.set_global_scales(0, global_scales(cfg, 0, "unit"))
+    print("bench: backing filled in %.1f s" % (time.time() - t0), file=sys.stderr, flush=True)
+    logits, _ = routing_trace(cfg, 0, steps=T)
+    xs = np.stack([activations(cfg, 0, t, 1) for t in range(T)])
+    d_logits = torch.from_numpy(logits[:, :1].copy()).to(dev)
+    d_x = torch.from_numpy(xs.view(np.int16)).to(dev)
+    d_y = torch.empty((T, 1, cfg.hidden), dtype=torch.float32, device=dev)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for t in range(W):
+        sc.decode(0, d_logits[t], d_x[t], d_y[t])
+    torch.cuda.synchronize()
+    st0 = sc.stats(0)
+    ev0 = sc.read_events(0)[1]
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        if not a.no_flush:
+            flush.add_(1.0)
+        sc.decode(0, d_logits[W + i], d_x[W + i], d_y[W + i], stream=stream, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_us = np.array([evs[i][0].elapsed_time(evs[i][5]) * 1e3 for i in range(K)])
+    phase_us = {p: np.array([evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(K)])
+                for j, p in enumerate(PHASES)}
+    st1 = sc.stats(0)
+    events, total = sc.read_events(0)
+    miss_steps = set(e[0] for e in events[len(events) - (total - ev0):]) if total > ev0 else set()
+    step_ids = [W + i for i in range(K)]   # the layer's step counter during timed step i
+    allhit = np.array([step_us[i] for i in range(K) if step_ids[i] not in miss_steps])
+    lookups = st1["lookups"] - st0["lookups"]
+    hits = st1["hits"] - st0["hits"]
+    misses = st1["misses"] - st0["misses"]
+    filled = st1["bytes_filled"] - st0["bytes_filled"]
+    fill_us = phase_us["fill"]
+    fill_time_miss = float(np.sum([fill_us[i] for i in range(K) if step_ids[i] in miss_steps]))
+
+    B = sc.blob_bytes
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    U = k  # M=1: the k picks are distinct experts
+    gateup_bytes = U * (2 * I * H // 2 + 2 * I * H // 16) + H * 2 + k * I * 4
+    down_bytes = U * (H * I // 2 + H * I // 16) + k * I * 4 + k * H * 4
+    gu = float(np.mean(phase_us["gateup"]))
+    dn = float(np.mean(phase_us["down"]))
+    src_hash = source_hash()
+    traffic = pmc_traffic("gateup_glm_m1", src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(float(np.mean(step_us)), 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(float(np.mean(step_us)) / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4e2m1*bf16->fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.description,
+            "routing": "Zipf(1.1) popularity, AR(0.99) drift, Gumbel top-k (seeded)",
+            "infinity_cache": "flushed between steps (512 MiB rewrite, not timed)" if not a.no_flush
+                              else "not flushed (back-to-back steps; repeats may hit the 256 MiB cache)",
+            "timing": "HIP events around each step's kernels on the launch stream",
+        },
+        "step_us": {"mean": float(np.mean(step_us)), "p10": float(np.percentile(step_us, 10)),
+                    "p50": float(np.percentile(step_us, 50)), "p90": float(np.percentile(step_us, 90)),
+                    "all_hit_mean": float(np.mean(allhit)) if allhit.size else None,
+                    "all_hit_steps": int(allhit.size)},
+        "kernels_us": {p: float(np.mean(v)) for p, v in phase_us.items()},
+        "lru": {"hit_rate": hits / lookups if lookups else None, "misses_per_step": misses / K,
+                "lookups": lookups, "hits": hits, "misses": misses},
+        "roofline": {
+            "kernel": KERNEL_NAMES["gateup"], "bound": "hbm",
+            "achieved": round(gateup_bytes / (gu * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gateup_bytes / (gu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": gu,
+        },
+        "down_gemv": {"kernel": KERNEL_NAMES["down"], "achieved_GBs": round(down_bytes / (dn * 1e-6) / 1e9, 1),
+                      "avg_launch_us": dn, "algorithmic_bytes_per_launch": down_bytes},
+        "host_link": {"bytes_filled": filled, "fill_us_on_miss_steps": fill_time_miss,
+                      "achieved_GBs": round(filled / (fill_time_miss * 1e-6) / 1e9, 2) if fill_time_miss > 0 else None,
+                      "peak_GBs": PCIE_PEAK_GBS},
+        "wall_s_timed_region": wall,
+    }
+    if not a.no_cpu_baseline:
+        print("bench: timing the oracle on a bounded CPU sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, logits, xs, W, a.cpu_baseline_steps)
+    sc.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

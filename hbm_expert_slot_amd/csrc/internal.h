@@ -1,0 +1,96 @@
+// Internal definitions shared by the host runtime and the kernels of libslotcache.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "slotcache.h"
+
+namespace sc {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxSlots = 1024;
+constexpr int kMaxRows = 256;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxPicks = 2048;        // max_rows * top_k
+constexpr int kRouteThreads = 256;
+constexpr int kGemvThreads = 256;
+constexpr int kCachedRows = SC_BYPASS_ROWS;
+
+enum Counter {
+  C_STEPS = 0, C_BYPASS, C_PICKS, C_LOOKUPS, C_HITS, C_MISSES, C_EVICT, C_FILLED, C_BYPASS_BYTES, C_N
+};
+
+// Workspace header words.
+enum Hdr { H_UNIQUE = 0, H_MISS = 1, H_BYPASS = 2, H_ROWS = 3, H_WORDS = 64 };
+
+// Device view of one layer: its maps, clock, counters, event ring, slots,
+// the backing bank it reads and that bank's global-scale table.
+struct LayerDev {
+  int32_t* e2s;            // [E]   slot of expert or -1
+  int32_t* s2e;            // [S]   expert in slot or -1
+  int64_t* key;            // [S]   LRU clock stamp, -1 = empty
+  int64_t* step;           // step counter
+  uint64_t* counters;      // [C_N]
+  uint32_t* error;         // device error word
+  uint64_t* ev_head;       // events ever logged
+  sc_event* events;        // [ev_cap] ring
+  uint8_t* slots;          // S blobs, stride blob_bytes
+  const uint8_t* backing;  // device-mapped view of the host bank, E blobs
+  const float* gs;         // [E][2] (w13, w2)
+  int32_t S;
+  int32_t ev_cap;
+};
+
+// Per-call scratch shared by all layers of a handle.
+struct Workspace {
+  int32_t* hdr;                 // [H_WORDS]
+  int32_t* pick_expert;         // [Pmax]  (row, rank) order
+  float* pick_w;                // [Pmax]
+  int32_t* pick_u;              // [Pmax]  unique index of each pick
+  int32_t* uniq_expert;         // [Pmax]
+  const uint8_t** uniq_ptr;     // [Pmax]  blob each unique expert is read from
+  float* uniq_gs;               // [Pmax][2]
+  int32_t* uniq_off;            // [Pmax + 1] CSR offsets into uniq_picks
+  int32_t* uniq_picks;          // [Pmax]  picks grouped by unique expert, ascending
+  const uint8_t** miss_src;     // [Pmax]
+  uint8_t** miss_dst;           // [Pmax]
+  float* h;                     // [Pmax][I]  SiLU(gate) * up, per pick
+  float* part;                  // [Pmax][H]  down projection, per pick
+};
+
+struct Shape {
+  int32_t H, I, E, k;
+  int64_t blob;                 // B_e
+  int64_t off_w13s, off_w2c, off_w2s;   // part offsets inside a blob
+};
+
+inline Shape make_shape(int H, int I, int E, int k) {
+  Shape s;
+  s.H = H; s.I = I; s.E = E; s.k = k;
+  int64_t w13c = (int64_t)2 * I * (H / 2);
+  int64_t w13s = (int64_t)2 * I * (H / 16);
+  int64_t w2c = (int64_t)H * (I / 2);
+  int64_t w2s = (int64_t)H * (I / 16);
+  s.off_w13s = w13c;
+  s.off_w2c = w13c + w13s;
+  s.off_w2s = w13c + w13s + w2c;
+  s.blob = w13c + w13s + w2c + w2s;
+  return s;
+}
+
+// True when the gate/up (K = H) or down (K = I) kernels are compiled for K.
+bool gemv_supported(int K, bool gateup);
+
+// Enqueue the phases of one step.  Each returns hipSuccess or the launch error.
+hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
+                        const float* logits, int M, hipStream_t st);
+hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st);
+hipError_t launch_gateup(const Shape& sh, const Workspace& W, const uint16_t* x, int M,
+                         hipStream_t st);
+hipError_t launch_down(const Shape& sh, const Workspace& W, int M, hipStream_t st);
+hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st);
+
+}  // namespace sc

@@ -1,0 +1,207 @@
+/*
+ * slotcache.h -- C ABI of the expert-slot MoE decode step for MI355X (gfx950).
+ *
+ * One MoE layer of an expert-offloaded mixture-of-experts model keeps S fixed
+ * HBM slots, each able to hold one routed expert; every expert of the layer
+ * lives in a pinned host backing store, and the slots are an LRU cache over
+ * it.  One decode step (moe_layer_decode) runs, all on the device and all
+ * enqueued on the caller's stream:
+ *   router top-k -> expert id to slot remap with LRU victim choice -> copy of
+ *   missed experts' weight and scale rows from host into their victim slots ->
+ *   routed gate/up and down products on NVFP4 weights with SiLU -> weighted
+ *   top-k combine.
+ * The method is the slot cache of the page "GLM 5.3 Testing: HBM Expert
+ * Allocation" (sections "What the slot cache is" and "The build, measured on a
+ * synthetic GLM-shaped layer"), with the LRU occupancy of the page "GB300 GLM
+ * 5.3 Testing" (section "Expert allocation vs a cache").
+ *
+ * Conventions.
+ *  - Every call returns sc_status: SC_OK (0) or a negative error; nothing
+ *    aborts or throws.  slotcache_last_error() gives a message for the last
+ *    non-OK status on the calling thread.
+ *  - Pointers named d_* are device pointers (hipMalloc / torch CUDA tensors);
+ *    pointers named h_* or host_* are host pointers.  `stream` is a
+ *    hipStream_t passed as void* (NULL = the null stream).
+ *  - The caller owns every device buffer (slot pool, state, workspace,
+ *    logits, x, y) and the stream.  The library owns the pinned host backing
+ *    store (allocated at the exact size, no power-of-two rounding) and frees
+ *    it in slotcache_destroy.
+ *  - Calls that use one handle must be ordered: the same stream, or streams
+ *    the caller synchronizes.  They share one workspace.
+ *
+ * Data formats (one expert "blob", B_e bytes; the same layout in a slot and in
+ * the backing store):
+ *   [w13 codes  2I x H/2 bytes] rows 0..I-1 gate, rows I..2I-1 up
+ *   [w13 scales 2I x H/16     ] one FP8 E4M3 (OCP "FN") per 16 K-elements
+ *   [w2 codes   H x I/2       ]
+ *   [w2 scales  H x I/16      ]
+ *   Codes are FP4 E2M1, two per byte, the even element in the low nibble.
+ *   Element value = e2m1(code) * e4m3(block scale) * global scale, with one
+ *   fp32 global scale per (expert, matrix) held in a device table.
+ *   B_e = 27*H*I/16 (21,233,664 B for H=6144, I=2048).
+ */
+#ifndef SLOTCACHE_H
+#define SLOTCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SC_API __attribute__((visibility("default")))
+#else
+#define SC_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SC_OK = 0,
+  SC_E_ARG = -1,          /* invalid argument or configuration; nothing enqueued */
+  SC_E_HOST_OOM = -2,     /* pinned host allocation failed */
+  SC_E_HIP = -3,          /* a HIP runtime call failed */
+  SC_E_STATE = -4,        /* call not valid in the handle's state */
+  SC_E_DEVICE = -5,       /* a device-side check latched an error word */
+  SC_E_UNSUPPORTED = -6   /* shape outside the compiled kernel set */
+} sc_status;
+
+typedef struct sc_handle sc_handle;
+
+/* Rows per step above which a step always reads the backing store directly
+ * (the prefill bypass; page "GLM 5.3 Testing: HBM Expert Allocation", section
+ * "What the slot cache is"). */
+#define SC_BYPASS_ROWS 16
+
+typedef struct {
+  int32_t n_layers;               /* >= 1 */
+  int32_t hidden;                 /* H: 256, 512, 1024, 2048, 4096, 6144 or 8192 */
+  int32_t inter;                  /* I: 128 ... 8192 (same set plus 128) */
+  int32_t n_experts;              /* E: top_k <= E <= 1024 */
+  int32_t top_k;                  /* k: 1 <= k <= 32 */
+  const int32_t* slots_per_layer; /* host [n_layers]; 1 <= S_l <= min(E, 1024) */
+  int32_t max_rows;               /* largest M the caller will pass, 1..256 */
+  int32_t n_banks;                /* host backing banks, 1..n_layers; layer l reads bank l % n_banks */
+  int32_t event_capacity;         /* per-layer miss-event ring, records (0 = 4096) */
+  uint32_t flags;                 /* reserved, must be 0 */
+} sc_config;
+
+typedef struct {
+  size_t blob_bytes;              /* B_e */
+  size_t slot_pool_bytes;         /* device: sum over layers of S_l * B_e; 256-B aligned base */
+  size_t state_bytes;             /* device: maps, LRU keys, counters, event rings, global scales */
+  size_t workspace_bytes;         /* device: per-call scratch shared by all layers */
+  size_t backing_bytes_per_bank;  /* host, allocated by the library: E * B_e */
+} sc_sizes;
+
+typedef struct {
+  uint64_t steps;         /* calls of moe_layer_decode on the layer */
+  uint64_t bypass_steps;  /* steps that read the backing store directly */
+  uint64_t picks;         /* M*k over cached steps */
+  uint64_t lookups;       /* unique experts over cached steps */
+  uint64_t hits;          /* unique experts already resident */
+  uint64_t misses;        /* unique experts copied into a slot */
+  uint64_t evictions;     /* misses whose victim slot held an expert */
+  uint64_t bytes_filled;  /* misses * B_e, host to HBM */
+  uint64_t bypass_bytes;  /* unique experts * B_e read from host by bypass steps */
+  uint32_t device_error;  /* nonzero: a device-side bounds check failed */
+  uint32_t reserved;
+} sc_stats;
+
+typedef struct {
+  int64_t step;     /* value of the layer's step counter when the miss happened */
+  int32_t expert;   /* expert copied in */
+  int32_t slot;     /* its slot */
+  int32_t evicted;  /* expert that held the slot, or -1 for an empty slot */
+  int32_t reserved;
+} sc_event;
+
+/* Sizes of the device buffers the caller must allocate for `cfg`.
+ * SC_E_ARG / SC_E_UNSUPPORTED for an invalid or unsupported configuration. */
+SC_API sc_status slotcache_query_sizes(const sc_config* cfg, sc_sizes* out);
+
+/* Binds caller-allocated device buffers (sizes from slotcache_query_sizes,
+ * 256-byte aligned), allocates the pinned backing store (n_banks * E * B_e
+ * bytes, exact size, device-mapped) and resets every layer to the cold state:
+ * all slots empty, keys -1, counters zero, global scales 1.0.  Synchronous.
+ * The device buffers must outlive the handle. */
+SC_API sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
+                         void* d_workspace, sc_handle** out);
+
+/* Host pointer and size of backing bank `bank` ([E][B_e] blobs, expert-major).
+ * The caller fills it before the first step that reads it and must not write
+ * it while steps are in flight. */
+SC_API sc_status slotcache_backing(sc_handle* h, int32_t bank, void** host_ptr, size_t* bytes);
+
+/* Copies the fp32 global scales of bank `bank` from host memory h_gs[E][2]
+ * ((w13, w2) per expert) to the device table.  Synchronous. */
+SC_API sc_status slotcache_set_global_scales(sc_handle* h, int32_t bank, const float* h_gs);
+
+/* Warm start for `layer`: slot s <- expert s for s < S (copied from the
+ * backing store), keys -1.  Synchronous.  With S == E this makes every
+ * expert resident (the all-resident layer). */
+SC_API sc_status slotcache_preload(sc_handle* h, int32_t layer);
+
+/* One decode step of `layer` for M rows (1 <= M <= max_rows):
+ *   d_logits fp32 [M][E], d_x bf16 bits [M][H], d_y fp32 [M][H] (written).
+ * Router: per row the k largest logits (ties -> lower expert id, NaN below
+ * -inf), weights = softmax over the k chosen logits.  Cached steps (M <= 16
+ * and at most S unique experts) remap, fill misses and compute from the
+ * slots; other steps leave the cache untouched and compute from the backing
+ * store.  Asynchronous on `stream`, no host synchronisation and no
+ * allocation, so it can be captured into a HIP graph (fixed addresses and
+ * shapes).  Argument errors return before anything is enqueued. */
+SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits,
+                           const uint16_t* d_x, int32_t M, float* d_y, void* stream);
+
+/* Phases of one step, for per-kernel timing. */
+#define SC_N_EVENTS 6
+/* moe_layer_decode plus hipEventRecord of events[i] (hipEvent_t passed as
+ * void*) before the routing kernel (0), after routing+remap (1), after the miss
+ * fill (2), after gate/up (3), after down (4) and after the combine (5).
+ * events == NULL is moe_layer_decode. */
+SC_API sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits,
+                              const uint16_t* d_x, int32_t M, float* d_y, void* stream,
+                              void* const* events);
+
+/* Counters of `layer`.  Synchronizes the stream of the last step. */
+SC_API sc_status slotcache_stats(sc_handle* h, int32_t layer, sc_stats* out);
+
+/* Slot map and LRU clock of `layer` (synchronizes): h_e2s int32[E] (slot or
+ * -1), h_s2e int32[S] (expert or -1), h_key int64[S] (-1 = empty), h_step
+ * (step counter).  Any output pointer may be NULL. */
+SC_API sc_status slotcache_read_state(sc_handle* h, int32_t layer, int32_t* h_e2s, int32_t* h_s2e,
+                               int64_t* h_key, int64_t* h_step);
+
+/* Restores a state read by slotcache_read_state (checkpoint / resume): checks
+ * that the maps are mutually inverse, copies the resident experts' blobs from
+ * the backing store into their slots and writes maps, keys and step counter.
+ * Counters and the event ring are left as they are.  Synchronous. */
+SC_API sc_status slotcache_write_state(sc_handle* h, int32_t layer, const int32_t* h_e2s,
+                                const int32_t* h_s2e, const int64_t* h_key, int64_t step);
+
+/* Miss events of `layer`, oldest first (synchronizes).  Copies up to `cap`
+ * records of the most recent min(total, event_capacity) into h_buf; *n_out =
+ * records copied, *total = events ever logged (total > event_capacity means
+ * the ring wrapped). */
+SC_API sc_status slotcache_read_events(sc_handle* h, int32_t layer, sc_event* h_buf, size_t cap,
+                                size_t* n_out, uint64_t* total);
+
+/* Routing of the most recent step (synchronizes): h_ids int32[M*k],
+ * h_w fp32[M*k] in (row, rank) order, *M_out = M, *bypass = 1 if the step
+ * bypassed the cache.  Outputs may be NULL. */
+SC_API sc_status slotcache_read_routing(sc_handle* h, int32_t* h_ids, float* h_w, int32_t* M_out,
+                                 int32_t* bypass);
+
+/* Message for the last non-OK status returned on this thread. */
+SC_API const char* slotcache_last_error(void);
+
+/* Frees the pinned backing store and the handle (synchronizes the device).
+ * The caller's device buffers are not freed. */
+SC_API void slotcache_destroy(sc_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLOTCACHE_H */

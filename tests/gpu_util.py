@@ -1,0 +1,82 @@
+"""Helpers for the GPU tests: build a bound SlotCache from a workload, run steps
+through the C ABI, and compare with the oracle on the same seeded inputs."""
+import functools
+import sys
+
+import numpy as np
+
+from synth import expert_blob, expert_blobs, global_scales
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        import pytest
+        pytest.skip("no GPU")
+    return torch
+
+
+def make_cache(cfg, n_layers=1, slots=None, max_rows=None, n_banks=1, gs_mode="unit",
+               event_capacity=0, n_experts=None):
+    from hbm_expert_slot_amd.cache import SlotCache
+    E = n_experts or cfg.n_experts
+    sc = SlotCache(n_layers, cfg.hidden, cfg.inter, E, cfg.top_k,
+                   slots if slots is not None else cfg.slots,
+                   max_rows or cfg.rows, n_banks, event_capacity)
+    for b in range(n_banks):
+        expert_blobs(cfg, b, range(E), out=sc.backing(b))
+        gs = global_scales(cfg, b, gs_mode)[:E]
+        sc.set_global_scales(b, gs)
+    return sc
+
+
+class OracleBlobs:
+    """Expert blobs regenerated from the seeded generator (never read back from the GPU side)."""
+
+    def __init__(self, cfg, bank=0, cache=48):
+        self.cfg, self.bank = cfg, bank
+        self.get = functools.lru_cache(maxsize=cache)(self._gen)
+
+    def _gen(self, e):
+        return expert_blob(self.cfg, self.bank, int(e))
+
+    def __call__(self, e):
+        return self.get(int(e))
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    d = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (d if d > 0 else 1.0))
+
+
+class GpuStepper:
+    """Runs moe_layer_decode on one layer with host inputs and returns host outputs."""
+
+    def __init__(self, sc, layer=0):
+        self.torch = torch_cuda()
+        self.sc, self.layer = sc, layer
+        self.n_events = 0
+
+    def step(self, logits, x_bits):
+        t = self.torch
+        M = logits.shape[0]
+        ld = t.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+        xd = t.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+        yd = t.empty((M, self.sc.hidden), dtype=t.float32, device="cuda")
+        self.sc.decode(self.layer, ld, xd, yd)
+        ids, w, byp = self.sc.read_routing()
+        return yd.cpu().numpy(), ids, w, byp
+
+    def new_events(self):
+        evs, total = self.sc.read_events(self.layer)
+        assert total <= 4096 or len(evs) == 4096
+        new = evs[len(evs) - (total - self.n_events):] if total > self.n_events else []
+        self.n_events = total
+        return new

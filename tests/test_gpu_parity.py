@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded inputs.  Slot bookkeeping (routing ids, miss/eviction events, slot maps,
+LRU keys, counters) must match bit for bit; routing weights to 1e-6 relative;
+outputs to relative L2 <= 1e-3 (fp32 accumulation against fp64)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import OracleLayer, route
+from synth import CONFIGS, WorkloadConfig, activations, global_scales, routing_trace
+
+from gpu_util import GpuStepper, OracleBlobs, log, make_cache, rel_l2, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-3
+W_TOL = 1e-6
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "lru_hand_trace.json")
+
+
+def _oracle_layer(cfg, S, gs_mode="unit", E=None):
+    E = E or cfg.n_experts
+    return OracleLayer(cfg.hidden, cfg.inter, E, cfg.top_k, S, OracleBlobs(cfg),
+                       global_scales(cfg, 0, gs_mode)[:E], keep_slot_bytes=False)
+
+
+def _check_step(t, gpu_out, orc, rec_events, want_y=True):
+    y_gpu, ids_gpu, w_gpu, byp_gpu, ev_gpu = gpu_out
+    y_o, rec, ids_o, w_o = orc
+    assert np.array_equal(ids_gpu, ids_o), (t, ids_gpu, ids_o)
+    np.testing.assert_allclose(w_gpu, w_o, rtol=W_TOL, atol=1e-7, err_msg="step %d" % t)
+    assert byp_gpu == rec.bypass, t
+    assert [tuple(e[1:]) for e in ev_gpu] == rec.events, (t, ev_gpu, rec.events)
+    assert all(e[0] == rec.step for e in ev_gpu)
+    if want_y:
+        r = rel_l2(y_gpu, y_o)
+        assert r <= Y_TOL, (t, r)
+        return r
+    return None
+
+
+def _check_state(sc, layer, st):
+    e2s, s2e, key, step = sc.read_state(layer)
+    assert list(e2s) == st.e2s
+    assert list(s2e) == st.s2e
+    assert list(key) == st.key
+    assert step == st.t
+
+
+def _check_counters(sc, layer, st):
+    c = sc.stats(layer)
+    oc = st.counters
+    for name in ("steps", "bypass_steps", "picks", "lookups", "hits", "misses", "evictions",
+                 "bytes_filled", "bypass_bytes"):
+        assert c[name] == getattr(oc, name), name
+    assert c["device_error"] == 0
+
+
+def _run_trace(cfg, sc, orc, steps, rows_fn, logits_fn, y_steps=None, state_every=1):
+    g = GpuStepper(sc)
+    worst = 0.0
+    for t in range(steps):
+        M = rows_fn(t)
+        z = logits_fn(t)[:M]
+        x = activations(cfg, 0, t, M)
+        want_y = y_steps is None or t in y_steps
+        y, ids, w, byp = g.step(z, x)
+        ev = g.new_events()
+        o = orc.decode(z, x, with_output=want_y)
+        r = _check_step(t, (y, ids, w, byp, ev), o, None, want_y)
+        if r is not None:
+            worst = max(worst, r)
+        if state_every and t % state_every == 0:
+            _check_state(sc, 0, orc.state)
+    _check_state(sc, 0, orc.state)
+    _check_counters(sc, 0, orc.state)
+    return worst
+
+
+@pytest.mark.parametrize("gs_mode", ["unit", "uniform"])
+def test_tiny_layer_all_steps(gs_mode):
+    cfg = CONFIGS["tiny"]
+    log("tiny parity gs=%s: 64 steps, H256 I128 E16 k2 S8" % gs_mode)
+    sc = make_cache(cfg, gs_mode=gs_mode)
+    orc = _oracle_layer(cfg, cfg.slots, gs_mode)
+    logits, rows = routing_trace(cfg, 0)
+    worst = _run_trace(cfg, sc, orc, cfg.steps, lambda t: 1, lambda t: logits[t])
+    log("tiny worst rel L2 %.3g, counters %s" % (worst, sc.stats(0)))
+    assert sc.stats(0)["evictions"] > 0
+    sc.close()
+
+
+def test_tiny_multi_row_steps():
+    """M in {2, 3, 4, 8, 16, 17, 32}: shared picks (union fetch), U > S bypass, M > 16 bypass."""
+    cfg = CONFIGS["tiny"]
+    log("tiny multi-row parity: M mix up to 32, S8")
+    sc = make_cache(cfg, max_rows=32)
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(123)
+    Ms = [2, 3, 4, 8, 16, 17, 32, 1, 4, 2]
+    zs = [rng.standard_normal((32, cfg.n_experts)).astype(np.float32) for _ in range(40)]
+    for t in range(40):
+        zs[t][:, :4] += 1.5          # shared favourites
+    worst = _run_trace(cfg, sc, orc, 40, lambda t: Ms[t % len(Ms)], lambda t: zs[t])
+    st = sc.stats(0)
+    log("multi-row worst rel L2 %.3g, stats %s" % (worst, st))
+    assert st["bypass_steps"] > 0 and st["misses"] > 0
+    sc.close()
+
+
+def test_hand_worked_trace_on_gpu():
+    g = json.load(open(GOLD))
+    base = CONFIGS["tiny"]
+    cfg = WorkloadConfig("hand", base.hidden, base.inter, g["n_experts"], g["top_k"], g["n_slots"],
+                         rows=2, steps=len(g["steps"]), seed=base.seed)
+    log("hand trace on GPU: E4 S2 k2")
+    sc = make_cache(cfg)
+    stepper = GpuStepper(sc)
+    for t, s in enumerate(g["steps"]):
+        ids = np.array(s["ids"])
+        z = np.zeros((ids.shape[0], g["n_experts"]), np.float32)
+        for m in range(ids.shape[0]):
+            for j, e in enumerate(ids[m]):
+                z[m, e] = 10.0 - j
+        y, gids, w, byp = stepper.step(z, activations(cfg, 0, t, ids.shape[0]))
+        assert np.array_equal(gids, ids)
+        assert byp == s["bypass"]
+        assert [list(e[1:]) for e in stepper.new_events()] == s["events"], t
+    e2s, s2e, key, step = sc.read_state(0)
+    f = g["final"]
+    assert list(e2s) == f["e2s"] and list(s2e) == f["s2e"] and list(key) == f["key"] and step == f["t"]
+    c = sc.stats(0)
+    for name, v in f["counters"].items():
+        assert c[name] == v, name
+    sc.close()
+
+
+def test_nonfinite_logits_route_like_the_oracle():
+    cfg = CONFIGS["tiny"]
+    log("non-finite logits routing")
+    sc = make_cache(cfg, max_rows=8)
+    orc = _oracle_layer(cfg, cfg.slots)
+    E = cfg.n_experts
+    rows = [
+        [np.nan] * 3 + [-np.inf] * 2 + [0.5] + [np.nan] * (E - 6),
+        [np.inf, 1.0, np.inf] + [0.0] * (E - 3),
+        [-np.inf] * (E - 1) + [np.nan],
+        [-0.0, 0.0] + [-1.0] * (E - 2),
+        [3.0] * E,
+    ]
+    z = np.array(rows, np.float32)
+    x = activations(cfg, 0, 0, len(rows))
+    y, ids, w, byp = GpuStepper(sc).step(z, x)
+    ids_o, w_o = route(z, cfg.top_k)
+    assert np.array_equal(ids, ids_o)
+    np.testing.assert_allclose(w, w_o, rtol=W_TOL, atol=0)
+    sc.close()
+
+
+def test_argument_errors_enqueue_nothing():
+    from hbm_expert_slot_amd import binding as B
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("argument errors")
+    sc = make_cache(cfg, max_rows=4)
+    z = torch.zeros((8, cfg.n_experts), dtype=torch.float32, device="cuda")
+    x = torch.zeros((8, cfg.hidden), dtype=torch.int16, device="cuda")
+    y = torch.zeros((8, cfg.hidden), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for layer, M, zp in ((0, 0, z.data_ptr()), (0, 5, z.data_ptr()), (1, 1, z.data_ptr()),
+                         (-1, 1, z.data_ptr()), (0, 1, None)):
+        with pytest.raises(B.SlotCacheError) as ei:
+            B.moe_layer_decode(sc.h, layer, zp, x.data_ptr(), M, y.data_ptr(), s)
+        assert ei.value.status == B.SC_E_ARG
+    assert sc.stats(0)["steps"] == 0
+    with pytest.raises(B.SlotCacheError):
+        sc.write_state(0, np.full(cfg.n_experts, -1), np.array([0] + [-1] * 7), np.full(8, -1), 0)
+    sc.close()
+
+
+def test_cached_layer_equals_all_resident_layer_bitwise():
+    """The pages' invariant, on the GPU: a churning 8-slot layer and a 16-slot
+    preloaded (all-resident) layer give bit-identical outputs on every step."""
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("cached vs all-resident bitwise: tiny, 2 layers (S=8, S=16 preloaded)")
+    sc = make_cache(cfg, n_layers=2, slots=[8, 16], max_rows=4, gs_mode="uniform")
+    sc.preload(1)
+    rng = np.random.default_rng(5)
+    for t in range(96):
+        M = 1 if t < 64 else 4
+        z = torch.from_numpy(rng.standard_normal((M, cfg.n_experts)).astype(np.float32)).cuda()
+        x = torch.from_numpy(activations(cfg, 0, t, M).view(np.int16)).cuda()
+        y0 = torch.empty((M, cfg.hidden), dtype=torch.float32, device="cuda")
+        y1 = torch.empty_like(y0)
+        sc.decode(0, z, x, y0)
+        sc.decode(1, z, x, y1)
+        assert torch.equal(y0, y1), t
+    s0, s1 = sc.stats(0), sc.stats(1)
+    log("cached layer stats %s / all-resident %s" % (s0, s1))
+    assert s0["evictions"] > 0 and s1["misses"] == 0
+    sc.close()
+
+
+def test_graph_replay_under_churn():
+    """One captured step replayed with new inputs each time (fixed addresses and
+    shapes), eager work and synchronisations in between, checked against the oracle."""
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("graph capture + replay under churn: tiny")
+    sc = make_cache(cfg)
+    orc = _oracle_layer(cfg, cfg.slots)
+    logits, _ = routing_trace(cfg, 0)
+    z = torch.zeros((1, cfg.n_experts), dtype=torch.float32, device="cuda")
+    x = torch.zeros((1, cfg.hidden), dtype=torch.int16, device="cuda")
+    y = torch.zeros((1, cfg.hidden), dtype=torch.float32, device="cuda")
+    # warm-up step outside the graph (also the first oracle step)
+    z.copy_(torch.from_numpy(logits[0, :1]))
+    x.copy_(torch.from_numpy(activations(cfg, 0, 0, 1).view(np.int16)))
+    sc.decode(0, z, x, y)
+    orc.decode(logits[0, :1], activations(cfg, 0, 0, 1), with_output=False)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        sc.decode(0, z, x, y, stream=s)
+        g.capture_end()
+    torch.cuda.synchronize()
+    stepper = GpuStepper(sc)
+    stepper.n_events = sc.read_events(0)[1]
+    for t in range(1, 40):
+        xb = activations(cfg, 0, t, 1)
+        z.copy_(torch.from_numpy(logits[t, :1]))
+        x.copy_(torch.from_numpy(xb.view(np.int16)))
+        g.replay()
+        torch.cuda.synchronize()
+        y_o, rec, ids_o, w_o = orc.decode(logits[t, :1], xb)
+        assert rel_l2(y.cpu().numpy(), y_o) <= Y_TOL, t
+        assert [tuple(e[1:]) for e in stepper.new_events()] == rec.events, t
+        _check_state(sc, 0, orc.state)
+        _ = (y * 2).sum().item()     # unrelated eager work between replays
+    _check_counters(sc, 0, orc.state)
+    sc.close()
+
+
+def test_checkpoint_resume_matches_a_continuous_run():
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("checkpoint / resume: tiny")
+    a = make_cache(cfg)
+    logits, _ = routing_trace(cfg, 0)
+    ga = GpuStepper(a)
+    for t in range(20):
+        ga.step(logits[t, :1], activations(cfg, 0, t, 1))
+    e2s, s2e, key, step = a.read_state(0)
+    b = make_cache(cfg)
+    b.write_state(0, e2s, s2e, key, step)
+    gb = GpuStepper(b)
+    for t in range(20, 50):
+        x = activations(cfg, 0, t, 1)
+        ya, ia, _, _ = ga.step(logits[t, :1], x)
+        yb, ib, _, _ = gb.step(logits[t, :1], x)
+        assert np.array_equal(ya, yb) and np.array_equal(ia, ib), t
+    for u, v in zip(a.read_state(0), b.read_state(0)):
+        assert np.array_equal(u, v)
+    a.close()
+    b.close()
+
+
+@pytest.mark.timeout(600)
+def test_glm_layer_300_steps():
+    """GLM-shaped layer at full size (H6144 I2048, 256 experts, top-8, S=128):
+    bookkeeping on all 300 steps, outputs on sampled steps (and every step's
+    output is checked for finiteness)."""
+    cfg = CONFIGS["glm"]
+    log("GLM parity: filling 256 x 21.2 MB backing")
+    sc = make_cache(cfg)
+    orc = _oracle_layer(cfg, cfg.slots)
+    logits, _ = routing_trace(cfg, 0)
+    sample = {0, 1, 2, 17, 128, 299}
+    log("GLM parity: 300 steps, y sampled at %s" % sorted(sample))
+    worst = _run_trace(cfg, sc, orc, cfg.steps, lambda t: 1, lambda t: logits[t], y_steps=sample,
+                       state_every=10)
+    st = sc.stats(0)
+    log("GLM worst rel L2 %.3g; hit rate %.3f; stats %s" % (worst, st["hits"] / st["lookups"], st))
+    sc.close()
+
+
+@pytest.mark.timeout(900)
+def test_glm_drafted_rounds_and_prefill_bypass():
+    """M=4 draft rounds, M=16 verify batches and M=64 prefill bypass on the GLM layer."""
+    cfg = CONFIGS["glm_draft"]
+    steps = 100
+    log("GLM drafted parity: filling backing; %d steps with M in {4, 16, 64}" % steps)
+    sc = make_cache(cfg)
+    orc = _oracle_layer(cfg, cfg.slots)
+    logits, rows = routing_trace(cfg, 0, steps=steps)
+    sample = {0, 9, 48, 49}     # M=4, M=16, M=4, M=64 (bypass)
+    worst = _run_trace(cfg, sc, orc, steps, lambda t: int(rows[t]), lambda t: logits[t], y_steps=sample,
+                       state_every=5)
+    st = sc.stats(0)
+    log("GLM drafted worst rel L2 %.3g; stats %s" % (worst, st))
+    assert st["bypass_steps"] == 2
+    sc.close()
