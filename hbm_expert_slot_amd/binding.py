@@ -18,7 +18,8 @@ SC_E_STATE = -4
 SC_E_DEVICE = -5
 SC_E_UNSUPPORTED = -6
 SC_BYPASS_ROWS = 16
-SC_N_EVENTS = 6
+SC_N_KERNELS = 5
+SC_N_EVENTS = 2 * SC_N_KERNELS
 
 EXPORTED = (
     "slotcache_query_sizes", "slotcache_init", "slotcache_backing", "slotcache_set_global_scales",

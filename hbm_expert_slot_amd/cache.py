@@ -58,7 +58,10 @@ class SlotCache:
         if events is None:
             B.moe_layer_decode(self.h, layer, logits.data_ptr(), x.data_ptr(), M, y.data_ptr(), s)
         else:
-            arr = (ctypes.c_void_p * B.SC_N_EVENTS)(*[ev.cuda_event for ev in events])
+            handles = [ev.cuda_event for ev in events]
+            if len(handles) != B.SC_N_EVENTS or not all(handles):
+                raise ValueError("need %d recorded (created) events" % B.SC_N_EVENTS)
+            arr = (ctypes.c_void_p * B.SC_N_EVENTS)(*handles)
             B.moe_layer_decode_ev(self.h, layer, logits.data_ptr(), x.data_ptr(), M, y.data_ptr(), s,
                                   ctypes.cast(arr, ctypes.c_void_p))
 

@@ -40,7 +40,8 @@ struct Geo {
 struct GemvArgs {
   const int32_t* hdr;
   const uint8_t* const* uniq_ptr;
-  const float* uniq_gs;
+  const int32_t* uniq_expert;
+  const float* gs;       // [E][2] global scales of the layer's bank
   const int32_t* uniq_off;
   const int32_t* uniq_picks;
   const void* operand;   // gate/up: bf16 x [M][H]; down: fp32 h [P][I]
@@ -53,6 +54,22 @@ struct GemvArgs {
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Loads through global-address-space pointers: blob pointers come from memory,
+// so without the cast the compiler emits flat loads (which also count against
+// the LDS counter and force conservative waits).  Device-mapped pinned host
+// memory is global memory to the GPU as well.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  const u32x4 v = *(g_u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *(g_u16*)(p); }
+
+// Wavefront index as a uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Widen the eight FP4 values of one dword (byte j holds elements 2j, 2j+1,
 // the even one in the low nibble) to bf16 or fp32 pairs.  The byte selector
@@ -128,154 +145,229 @@ __device__ __forceinline__ float seg_dot_f32(const uint4& q, uint32_t sc, const 
   return fmaf(b[1], s1, b[0] * s0);
 }
 
-template <int K, int MR, bool GATEUP>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
-  using G = Geo<K>;
-  constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
-  constexpr int OPW = GATEUP ? 16 : 32;   // operand words per lane per chunk
-  const int U = a.hdr[H_UNIQUE];
-  const int lane = threadIdx.x & 63;
-  const int seg = lane % LPR, rsub = lane / LPR;
-  const long nwaves = (long)gridDim.x * (kGemvThreads / 64);
-  const long gw = (long)blockIdx.x * (kGemvThreads / 64) + (threadIdx.x >> 6);
-  const int spu = a.rows / RPW;
-  const long items = (long)U * spu;
-  const long per = (items + nwaves - 1) / nwaves;
-  long it = gw * per;
-  const long end = items < it + per ? items : it + per;
+// Sum NV values per lane over the LPR lanes of a row group with a transposed
+// butterfly: while more than one value is left, each step trades half of the
+// values with the partner lane, so a lane ends up holding the group sum of one
+// value, index (lane % LPR) / (LPR / NV).
+template <int O, int C>
+struct XRed {
+  __device__ static __forceinline__ void run(float* v, int lane) {
+    if constexpr (O == 0) {
+      return;
+    } else if constexpr (C > 1) {
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < C / 2; ++i) {
+        const float send = up ? v[i] : v[i + C / 2];
+        const float keep = up ? v[i + C / 2] : v[i];
+        v[i] = keep + __shfl_xor(send, O);
+      }
+      XRed<O / 2, C / 2>::run(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], O);
+      XRed<O / 2, 1>::run(v, lane);
+    }
+  }
+};
 
-  while (it < end) {
-    const int u = (int)(it / spu);
-    const long uend = end < (long)(u + 1) * spu ? end : (long)(u + 1) * spu;
-    const uint8_t* blob = a.uniq_ptr[u];
-    const float gs = a.uniq_gs[2 * u + (GATEUP ? 0 : 1)];
-    const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
-    for (int c0 = off0; c0 < off1; c0 += MR) {
-      const int nc = off1 - c0 < MR ? off1 - c0 : MR;
-      int pk[MR];
-      uint32_t opw[MR][NSEG][OPW];
+// Streaming GEMV.  Each unique expert's row steps are split into `wpu`
+// contiguous runs, one per wavefront (task); a wavefront keeps the operand
+// slices of up to MR picks in registers and walks its run R row steps at a
+// time with the next R steps' code and scale loads issued before the current
+// ones are consumed (register double buffering), so every wavefront always has
+// two groups of loads in flight.
+template <int K, int MR, int R, bool GATEUP, bool STRIDED>
+struct Gemv {
+  using G = Geo<K>;
+  static constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
+  static constexpr int OPW = GATEUP ? 16 : 32;
+  static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int NV = R * MR;
+  static_assert(NV <= LPR, "too many values for the row group");
+
+  struct Buf {
+    uint4 q[R][NM][NSEG];
+    uint32_t sc[R][NM][NSEG];
+  };
+
+  // Row step of the task's i-th step: base + i * stride.
+  __device__ static __forceinline__ void load(Buf& b, const uint8_t* code_base, const uint8_t* scale_base,
+                                              int i, int n, int base, int stride, int rsub, int up_row0) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const bool ok = i + j < n;
+      const int r = (base + (i + j) * stride) * RPW + rsub;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const size_t row = (size_t)(r + m * up_row0);
+#pragma unroll
+        for (int c = 0; c < NSEG; ++c) {
+          if (ok) {
+            b.q[j][m][c] = ld16(code_base + row * (K / 2) + c * 1024);
+            b.sc[j][m][c] = ld2(scale_base + row * (K / 16) + c * 128);
+          } else {
+            b.q[j][m][c] = make_uint4(0u, 0u, 0u, 0u);
+            b.sc[j][m][c] = 0u;
+          }
+        }
+      }
+    }
+  }
+
+  __device__ static __forceinline__ void process(const Buf& b, const uint32_t (&opw)[MR][NSEG][OPW],
+                                                 const int (&pk)[MR], int nc, int i, int n, int base,
+                                                 int stride, int lane, int rsub, float gs, const GemvArgs& a) {
+    float v0[NV], v1[NV];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
 #pragma unroll
       for (int mi = 0; mi < MR; ++mi) {
-        pk[mi] = mi < nc ? a.uniq_picks[c0 + mi] : 0;
+        float acc0 = 0.0f, acc1 = 0.0f;
         if (mi < nc) {
+#pragma unroll
+          for (int c = 0; c < NSEG; ++c) {
+            if (GATEUP) {
+              acc0 += seg_dot_bf16(b.q[j][0][c], b.sc[j][0][c], opw[mi][c]);
+              acc1 += seg_dot_bf16(b.q[j][NM - 1][c], b.sc[j][NM - 1][c], opw[mi][c]);
+            } else {
+              acc0 += seg_dot_f32(b.q[j][0][c], b.sc[j][0][c], reinterpret_cast<const float*>(opw[mi][c]));
+            }
+          }
+        }
+        v0[j * MR + mi] = acc0;
+        v1[j * MR + mi] = acc1;
+      }
+    }
+    XRed<LPR / 2, NV>::run(v0, lane);
+    if (GATEUP) XRed<LPR / 2, NV>::run(v1, lane);
+    const int g = lane % LPR;
+    if (g % (LPR / NV) == 0) {
+      const int idx = g / (LPR / NV);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi) {
+          if (idx == j * MR + mi && mi < nc && i + j < n) {
+            const int r = (base + (i + j) * stride) * RPW + rsub;
+            a.out[(size_t)pk[mi] * a.rows + r] =
+                GATEUP ? silu_f32(v0[0] * gs) * (v1[0] * gs) : v0[0] * gs;
+          }
+        }
+      }
+    }
+  }
+
+  __device__ static __forceinline__ void run(const GemvArgs& a) {
+    const int U = a.hdr[H_UNIQUE];
+    const int lane = threadIdx.x & 63;
+    const int seg = lane % LPR, rsub = lane / LPR;
+    const int nwaves = gridDim.x * (kGemvThreads / 64);
+    const int gw = blockIdx.x * (kGemvThreads / 64) + wave_id();
+    const int spu = a.rows / RPW;
+    int wpu = nwaves / U;
+    if (wpu < 1) wpu = 1;
+    if (wpu > spu) wpu = spu;
+    const int per = (spu + wpu - 1) / wpu;
+    const int ntask = U * wpu;
+    for (int task = gw; task < ntask; task += nwaves) {
+      const int u = task / wpu, sub = task - (task / wpu) * wpu;
+      // a task owns row steps base + i * stride, i < n
+      int base, stride, n;
+      if (STRIDED) {
+        base = sub;
+        stride = wpu;
+        n = (spu - sub + wpu - 1) / wpu;
+      } else {
+        base = sub * per;
+        stride = 1;
+        n = spu - base < per ? spu - base : per;
+      }
+      if (n <= 0) continue;
+      const uint8_t* blob = a.uniq_ptr[u];
+      const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
+      const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
+      const uint8_t* code_base = blob + a.code_off + seg * 16;
+      const uint8_t* scale_base = blob + a.scale_off + seg * 2;
+      for (int c0 = off0; c0 < off1; c0 += MR) {
+        const int nc = off1 - c0 < MR ? off1 - c0 : MR;
+        Buf A, B;
+        load(A, code_base, scale_base, 0, n, base, stride, rsub, a.up_row0);
+        int pk[MR];
+        uint32_t opw[MR][NSEG][OPW];
+#pragma unroll
+        for (int mi = 0; mi < MR; ++mi) {
+          pk[mi] = mi < nc ? a.uniq_picks[c0 + mi] : 0;
 #pragma unroll
           for (int c = 0; c < NSEG; ++c) {
             const int e0 = c * 2048 + seg * 32;
             const uint4* src;
-            if (GATEUP) {
-              const int m = pk[mi] / a.k;
+            if (GATEUP)
               src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.operand) +
-                                                   (size_t)m * K + e0);
-            } else {
+                                                   (size_t)(pk[mi] / a.k) * K + e0);
+            else
               src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.operand) +
                                                    (size_t)pk[mi] * K + e0);
-            }
 #pragma unroll
             for (int v = 0; v < OPW / 4; ++v) {
-              uint4 t = src[v];
+              uint4 t = mi < nc ? src[v] : make_uint4(0u, 0u, 0u, 0u);
               opw[mi][c][4 * v + 0] = t.x;
               opw[mi][c][4 * v + 1] = t.y;
               opw[mi][c][4 * v + 2] = t.z;
               opw[mi][c][4 * v + 3] = t.w;
             }
           }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NSEG; ++c)
-#pragma unroll
-            for (int v = 0; v < OPW; ++v) opw[mi][c][v] = 0u;
         }
-      }
-      for (long i2 = it; i2 < uend; ++i2) {
-        const int r = (int)(i2 - (long)u * spu) * RPW + rsub;
-        if (GATEUP) {
-          const uint8_t* cg = blob + a.code_off + (size_t)r * (K / 2) + seg * 16;
-          const uint8_t* cu = blob + a.code_off + (size_t)(a.up_row0 + r) * (K / 2) + seg * 16;
-          const uint8_t* sg = blob + a.scale_off + (size_t)r * (K / 16) + seg * 2;
-          const uint8_t* su = blob + a.scale_off + (size_t)(a.up_row0 + r) * (K / 16) + seg * 2;
-          uint4 qg[NSEG], qu[NSEG];
-          uint32_t scg[NSEG], scu[NSEG];
-#pragma unroll
-          for (int c = 0; c < NSEG; ++c) {
-            qg[c] = *reinterpret_cast<const uint4*>(cg + c * 1024);
-            qu[c] = *reinterpret_cast<const uint4*>(cu + c * 1024);
-            scg[c] = *reinterpret_cast<const uint16_t*>(sg + c * 128);
-            scu[c] = *reinterpret_cast<const uint16_t*>(su + c * 128);
-          }
-          float ag[MR], au[MR];
-#pragma unroll
-          for (int mi = 0; mi < MR; ++mi) {
-            ag[mi] = 0.0f;
-            au[mi] = 0.0f;
-            if (mi < nc) {
-#pragma unroll
-              for (int c = 0; c < NSEG; ++c) {
-                ag[mi] += seg_dot_bf16(qg[c], scg[c], opw[mi][c]);
-                au[mi] += seg_dot_bf16(qu[c], scu[c], opw[mi][c]);
-              }
-            }
-            ag[mi] = group_sum<LPR>(ag[mi]);
-            au[mi] = group_sum<LPR>(au[mi]);
-          }
-          if (seg == 0) {
-#pragma unroll
-            for (int mi = 0; mi < MR; ++mi)
-              if (mi < nc)
-                a.out[(size_t)pk[mi] * a.rows + r] = silu_f32(ag[mi] * gs) * (au[mi] * gs);
-          }
-        } else {
-          const uint8_t* cd = blob + a.code_off + (size_t)r * (K / 2) + seg * 16;
-          const uint8_t* sd = blob + a.scale_off + (size_t)r * (K / 16) + seg * 2;
-          uint4 qd[NSEG];
-          uint32_t scd[NSEG];
-#pragma unroll
-          for (int c = 0; c < NSEG; ++c) {
-            qd[c] = *reinterpret_cast<const uint4*>(cd + c * 1024);
-            scd[c] = *reinterpret_cast<const uint16_t*>(sd + c * 128);
-          }
-          float ad[MR];
-#pragma unroll
-          for (int mi = 0; mi < MR; ++mi) {
-            ad[mi] = 0.0f;
-            if (mi < nc) {
-#pragma unroll
-              for (int c = 0; c < NSEG; ++c)
-                ad[mi] += seg_dot_f32(qd[c], scd[c], reinterpret_cast<const float*>(opw[mi][c]));
-            }
-            ad[mi] = group_sum<LPR>(ad[mi]);
-          }
-          if (seg == 0) {
-#pragma unroll
-            for (int mi = 0; mi < MR; ++mi)
-              if (mi < nc) a.out[(size_t)pk[mi] * a.rows + r] = ad[mi] * gs;
-          }
+        int i = 0;
+        while (true) {
+          if (i + R < n) load(B, code_base, scale_base, i + R, n, base, stride, rsub, a.up_row0);
+          process(A, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a);
+          i += R;
+          if (i >= n) break;
+          if (i + R < n) load(A, code_base, scale_base, i + R, n, base, stride, rsub, a.up_row0);
+          process(B, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a);
+          i += R;
+          if (i >= n) break;
         }
       }
     }
-    it = uend;
   }
+};
+
+template <int K, int MR, int R, bool GATEUP, bool STRIDED>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+  Gemv<K, MR, R, GATEUP, STRIDED>::run(a);
 }
 
+// Copies the step's missed blobs (host-mapped pinned memory -> HBM slots).
+// The misses' 16-byte chunks form one index space so every thread keeps
+// four loads in flight across blob boundaries; with no misses it exits.
+// Entries whose destination is null (a miss the remap could not place) are
+// skipped.
 __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t* const* src,
                                                uint8_t* const* dst, long n16) {
-  const int nmiss = hdr[H_MISS];
+  const long total = (long)hdr[H_MISS] * n16;
   const long stride = (long)gridDim.x * blockDim.x;
-  const long t0 = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int i = 0; i < nmiss; ++i) {
-    const uint4* s = reinterpret_cast<const uint4*>(src[i]);
-    uint4* d = reinterpret_cast<uint4*>(dst[i]);
-    long o = t0;
-    for (; o + 3 * stride < n16; o += 4 * stride) {   // four 16-byte loads in flight
-      const uint4 v0 = s[o], v1 = s[o + stride], v2 = s[o + 2 * stride], v3 = s[o + 3 * stride];
-      d[o] = v0;
-      d[o + stride] = v1;
-      d[o + 2 * stride] = v2;
-      d[o + 3 * stride] = v3;
+  long o = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; o + 3 * stride < total; o += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long g = o + j * stride, i = g / n16;
+      if (dst[i]) v[j] = ld16(src[i] + (g - i * n16) * 16);
     }
-    for (; o < n16; o += stride) d[o] = s[o];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long g = o + j * stride, i = g / n16;
+      if (dst[i]) *reinterpret_cast<uint4*>(dst[i] + (g - i * n16) * 16) = v[j];
+    }
+  }
+  for (; o < total; o += stride) {
+    const long i = o / n16;
+    if (dst[i]) *reinterpret_cast<uint4*>(dst[i] + (o - i * n16) * 16) = ld16(src[i] + (o - i * n16) * 16);
   }
 }
 
+// y[m][r] = sum over j = 0..k-1 of w[m][j] * part[m*k + j][r], in rank order.
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* w, float* y,
                                                   int M, int k, int H) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
@@ -288,30 +380,51 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
 
 typedef void (*GemvFn)(GemvArgs);
 
+// Row steps per pipeline stage: as many as the row group can reduce at once, at most 8 for down, 1 for gate/up.
+template <int K, int MR, bool GATEUP>
+constexpr int stage_rows() {
+  constexpr int lim = Geo<K>::LPR / MR;
+  constexpr int want = GATEUP ? 1 : 8;
+  return want < lim ? want : lim;
+}
+
+template <int K, int MR, bool GATEUP>
+GemvFn gemv_fn() {
+  return k_gemv<K, MR, stage_rows<K, MR, GATEUP>(), GATEUP, false>;
+}
+
 template <bool GATEUP, int MR>
 GemvFn pick_gemv(int K) {
   switch (K) {
-    case 128: return GATEUP ? nullptr : k_gemv<128, MR, GATEUP>;
-    case 256: return k_gemv<256, MR, GATEUP>;
-    case 512: return k_gemv<512, MR, GATEUP>;
-    case 1024: return k_gemv<1024, MR, GATEUP>;
-    case 2048: return k_gemv<2048, MR, GATEUP>;
-    case 4096: return k_gemv<4096, MR, GATEUP>;
-    case 6144: return k_gemv<6144, MR, GATEUP>;
-    case 8192: return k_gemv<8192, MR, GATEUP>;
+    case 128: return GATEUP ? nullptr : gemv_fn<128, MR, GATEUP>();
+    case 256: return gemv_fn<256, MR, GATEUP>();
+    case 512: return gemv_fn<512, MR, GATEUP>();
+    case 1024: return gemv_fn<1024, MR, GATEUP>();
+    case 2048: return gemv_fn<2048, MR, GATEUP>();
+    case 4096: return gemv_fn<4096, MR, GATEUP>();
+    case 6144: return gemv_fn<6144, MR, GATEUP>();
+    case 8192: return gemv_fn<8192, MR, GATEUP>();
     default: return nullptr;
   }
 }
 
 int rows_per_wave(int K) { return K >= 2048 ? 1 : 2048 / K; }
+int stage_rows_rt(int K, int MR, bool gateup) {
+  const int lpr = K >= 2048 ? 64 : K / 32;
+  const int want = gateup ? 1 : 8;
+  return want < lpr / MR ? want : lpr / MR;
+}
 
-int gemv_blocks(long items) {
-  long waves = (items + 3) / 4;   // at least four row-steps per wavefront
-  long blocks = (waves + 3) / 4;
+// Enough wavefronts for about two pipeline stages each, capped per kernel.
+int gemv_blocks(long stages, int cap) {
+  long blocks = (stages + 7) / 8;
   if (blocks < 1) blocks = 1;
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > cap) blocks = cap;
   return (int)blocks;
 }
+
+constexpr int kGateupBlocks = 1024;
+constexpr int kDownBlocks = 512;
 
 int mr_for(int M) { return M == 1 ? 1 : 2; }
 
@@ -321,20 +434,25 @@ bool gemv_supported(int K, bool gateup) {
   return gateup ? pick_gemv<true, 1>(K) != nullptr : pick_gemv<false, 1>(K) != nullptr;
 }
 
-hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill, dim3(512), dim3(256), 0, st, W.hdr, W.miss_src, W.miss_dst,
-                     (long)(sh.blob / 16));
-  return hipGetLastError();
+hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev) {
+  return sc_launch(k_fill, dim3(1024), dim3(256), st, ev, (const int32_t*)W.hdr,
+                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16));
 }
 
-hipError_t launch_gateup(const Shape& sh, const Workspace& W, const uint16_t* x, int M,
-                         hipStream_t st) {
+static GemvArgs base_args(const Workspace& W, const float* gs) {
   GemvArgs a;
   a.hdr = W.hdr;
   a.uniq_ptr = W.uniq_ptr;
-  a.uniq_gs = W.uniq_gs;
+  a.uniq_expert = W.uniq_expert;
+  a.gs = gs;
   a.uniq_off = W.uniq_off;
   a.uniq_picks = W.uniq_picks;
+  return a;
+}
+
+hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
+                         hipStream_t st, KEvents ev) {
+  GemvArgs a = base_args(W, gs);
   a.operand = x;
   a.out = W.h;
   a.rows = sh.I;
@@ -346,18 +464,13 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const uint16_t* x,
   GemvFn fn = mr == 1 ? pick_gemv<true, 1>(sh.H) : pick_gemv<true, 2>(sh.H);
   if (!fn) return hipErrorInvalidValue;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  const int blocks = gemv_blocks(maxu * (sh.I / rows_per_wave(sh.H)));
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(kGemvThreads), 0, st, a);
-  return hipGetLastError();
+  const long stages = maxu * (sh.I / rows_per_wave(sh.H)) / stage_rows_rt(sh.H, mr, true);
+  return sc_launch(fn, dim3(gemv_blocks(stages, kGateupBlocks)), dim3(kGemvThreads), st, ev, a);
 }
 
-hipError_t launch_down(const Shape& sh, const Workspace& W, int M, hipStream_t st) {
-  GemvArgs a;
-  a.hdr = W.hdr;
-  a.uniq_ptr = W.uniq_ptr;
-  a.uniq_gs = W.uniq_gs;
-  a.uniq_off = W.uniq_off;
-  a.uniq_picks = W.uniq_picks;
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, hipStream_t st,
+                       KEvents ev) {
+  GemvArgs a = base_args(W, gs);
   a.operand = W.h;
   a.out = W.part;
   a.rows = sh.H;
@@ -369,16 +482,15 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, int M, hipStream_t s
   GemvFn fn = mr == 1 ? pick_gemv<false, 1>(sh.I) : pick_gemv<false, 2>(sh.I);
   if (!fn) return hipErrorInvalidValue;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  const int blocks = gemv_blocks(maxu * (sh.H / rows_per_wave(sh.I)));
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(kGemvThreads), 0, st, a);
-  return hipGetLastError();
+  const long stages = maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, mr, false);
+  return sc_launch(fn, dim3(gemv_blocks(stages, kDownBlocks)), dim3(kGemvThreads), st, ev, a);
 }
 
-hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st) {
+hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,
+                          KEvents ev) {
   const long n = (long)M * sh.H;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, W.part,
-                     W.pick_w, y, M, sh.k, sh.H);
-  return hipGetLastError();
+  return sc_launch(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), st, ev, (const float*)W.part,
+                   (const float*)W.pick_w, y, M, sh.k, sh.H);
 }
 
 }  // namespace sc

@@ -1,6 +1,7 @@
 // Internal definitions shared by the host runtime and the kernels of libslotcache.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -52,7 +53,6 @@ struct Workspace {
   int32_t* pick_u;              // [Pmax]  unique index of each pick
   int32_t* uniq_expert;         // [Pmax]
   const uint8_t** uniq_ptr;     // [Pmax]  blob each unique expert is read from
-  float* uniq_gs;               // [Pmax][2]
   int32_t* uniq_off;            // [Pmax + 1] CSR offsets into uniq_picks
   int32_t* uniq_picks;          // [Pmax]  picks grouped by unique expert, ascending
   const uint8_t** miss_src;     // [Pmax]
@@ -81,16 +81,34 @@ inline Shape make_shape(int H, int I, int E, int k) {
   return s;
 }
 
+// Optional start/stop events of one launch (both null: a plain launch).  With
+// events the kernel is launched through hipExtLaunchKernelGGL, which stamps
+// the events at the kernel's own start and end.
+struct KEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename F, typename... Args>
+inline hipError_t sc_launch(F kernel, dim3 grid, dim3 block, hipStream_t st, KEvents ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
+}
+
 // True when the gate/up (K = H) or down (K = I) kernels are compiled for K.
 bool gemv_supported(int K, bool gateup);
 
 // Enqueue the phases of one step.  Each returns hipSuccess or the launch error.
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
-                        const float* logits, int M, hipStream_t st);
-hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st);
-hipError_t launch_gateup(const Shape& sh, const Workspace& W, const uint16_t* x, int M,
-                         hipStream_t st);
-hipError_t launch_down(const Shape& sh, const Workspace& W, int M, hipStream_t st);
-hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st);
+                        const float* logits, int M, hipStream_t st, KEvents ev);
+hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev);
+hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
+                         hipStream_t st, KEvents ev);
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, hipStream_t st,
+                       KEvents ev);
+hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,
+                          KEvents ev);
 
 }  // namespace sc

@@ -40,19 +40,74 @@ __device__ __forceinline__ uint64_t order_key(float z, int e) {
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+// Cross-lane reductions on the DPP path (no LDS round trip): quad
+// permutations and the half-row / row mirrors reduce each 16-lane row, two
+// row broadcasts fold the rows into lane 63, which readlane makes uniform.
+// Lanes of a row that the row mask leaves out read `OLD` instead of a
+// neighbour: the identity of the reduction (0 for max and sum, all ones for min).
+template <int CTRL, int ROWS, uint32_t OLD = 0u>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)OLD, (int)v, CTRL, ROWS, 0xF, false);
 }
 
+template <bool MAX, int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_step_u64(uint64_t v) {
+  constexpr uint32_t ID = MAX ? 0u : 0xFFFFFFFFu;
+  const uint64_t o = ((uint64_t)dpp_u32<CTRL, ROWS, ID>((uint32_t)(v >> 32)) << 32) |
+                     dpp_u32<CTRL, ROWS, ID>((uint32_t)v);
+  if (MAX) return o > v ? o : v;
+  return o < v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Max (MAX) or min over the wavefront, returned as a uniform value.
+template <bool MAX>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v) {
+  v = dpp_step_u64<MAX, 0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_step_u64<MAX, 0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_step_u64<MAX, 0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_step_u64<MAX, 0x140, 0xF>(v);   // row_mirror
+  v = dpp_step_u64<MAX, 0x142, 0xA>(v);   // row_bcast:15 -> rows 1, 3
+  v = dpp_step_u64<MAX, 0x143, 0xC>(v);   // row_bcast:31 -> rows 2, 3
+  return readlane_u64(v, 63);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = dpp_u32<CTRL, ROWS>(v);
+  return o > v ? o : v;
+}
+
+// Unsigned 32-bit maximum over the wavefront, uniform result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32<0xB1, 0xF>(v);
+  v = dpp_max_u32<0x4E, 0xF>(v);
+  v = dpp_max_u32<0x141, 0xF>(v);
+  v = dpp_max_u32<0x140, 0xF>(v);
+  v = dpp_max_u32<0x142, 0xA>(v);
+  v = dpp_max_u32<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_f32(float v) {
+  return v + __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v)));
+}
+
+// Sum over the wavefront in a fixed order, returned as a uniform value.
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v = dpp_add_f32<0xB1, 0xF>(v);
+  v = dpp_add_f32<0x4E, 0xF>(v);
+  v = dpp_add_f32<0x141, 0xF>(v);
+  v = dpp_add_f32<0x140, 0xF>(v);
+  v = dpp_add_f32<0x142, 0xA>(v);
+  v = dpp_add_f32<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Exclusive rank of `pred` among the block's threads in thread order.
@@ -117,66 +172,120 @@ struct RouteArgs {
   int M;
 };
 
+// Router for one row on one wavefront: lane l holds the keys of experts
+// l, l+64, ... sorted by (logit descending, id ascending).  Each round takes
+// the wavefront maximum of the lanes' head order words (32-bit); equal heads
+// are settled by the lowest expert id, and the owner lane pops its head.
+// Lane j < k returns the j-th pick and its logit.
+template <int EPL>
+__device__ __forceinline__ void route_row(const float* z, int E, int k, int lane, int* pick, float* logit) {
+  uint64_t keys[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    keys[i] = e < E ? order_key(z[e], e) : 0ull;
+  }
+#pragma unroll
+  for (int i = 1; i < EPL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j)
+      if (keys[j] > keys[j - 1]) {
+        const uint64_t tmp = keys[j];
+        keys[j] = keys[j - 1];
+        keys[j - 1] = tmp;
+      }
+  int my_e = 0;
+  uint32_t my_ord = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t h_ord = (uint32_t)(keys[0] >> 32);
+    const uint32_t h_inv = (uint32_t)keys[0];            // 0xFFFFFFFF - expert id
+    const uint32_t best = wave_max_u32(h_ord);
+    const uint64_t tied = __ballot(keys[0] != 0ull && h_ord == best);
+    uint32_t win_inv;
+    if (__popcll(tied) == 1) {
+      win_inv = (uint32_t)__builtin_amdgcn_readlane((int)h_inv, (int)__ffsll((unsigned long long)tied) - 1);
+    } else {
+      win_inv = wave_max_u32(((tied >> lane) & 1ull) ? h_inv : 0u);   // lowest id among the tied heads
+    }
+    if (keys[0] != 0ull && h_ord == best && h_inv == win_inv) {
+#pragma unroll
+      for (int i = 0; i + 1 < EPL; ++i) keys[i] = keys[i + 1];
+      keys[EPL - 1] = 0ull;
+    }
+    if (lane == j) {
+      my_e = (int)(0xFFFFFFFFu - win_inv);
+      my_ord = best;
+    }
+  }
+  // the logit back from its order key (NaN keys carry ord 1; -0 was folded into +0)
+  const uint32_t zb = (my_ord & 0x80000000u) ? (my_ord & 0x7FFFFFFFu) : ~my_ord;
+  *pick = my_e;
+  *logit = my_ord == 1u ? __uint_as_float(0x7FC00000u) : __uint_as_float(zb);
+}
+
+template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
+  constexpr int SPT = kMaxSlots / kRouteThreads;   // slots per thread
   __shared__ int s_pick[kMaxPicks];
-  __shared__ int s_first[kMaxExperts];
+  __shared__ int s_first[kMaxExperts];   // first pick position per expert; later pick counts
   __shared__ int s_last[kMaxExperts];
   __shared__ int s_uidx[kMaxExperts];
   __shared__ int s_uexp[kMaxExperts];
   __shared__ int s_uslot[kMaxExperts];
-  __shared__ int s_umiss[kMaxExperts];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ int s_off[kMaxExperts];
-  __shared__ int s_ref[kMaxSlots];
+  __shared__ int s_umiss[kMaxExperts];   // miss rank per unique; later CSR offsets
   __shared__ int s_victim[kMaxSlots];
-  __shared__ long long s_ckey[kMaxSlots];
+  __shared__ int s_e2s[kMaxExperts];     // snapshot of the slot map
+  __shared__ int s_s2e[kMaxSlots];
+  __shared__ long long s_key[kMaxSlots]; // snapshot of the clock, then candidate keys
+  __shared__ uint8_t s_ref[kMaxSlots];
   __shared__ int s_wc[kRouteThreads / 64];
+  __shared__ unsigned long long s_wmin[kRouteThreads / 64];
   __shared__ int s_nevict;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.sh.E, k = a.sh.k, M = a.M, S = a.L.S;
   const int P = M * k;
   const int64_t t = *a.L.step;
   const uint64_t ev_head = *a.L.ev_head;
+  uint64_t cnt[C_N];
+  if (tid == 0) {
+#pragma unroll
+    for (int c = 0; c < C_N; ++c) cnt[c] = a.L.counters[c];
+  }
+
+  // Snapshot the layer state into LDS; these loads overlap the logits loads.
+  for (int e = tid; e < E; e += kRouteThreads) {
+    s_e2s[e] = a.L.e2s[e];
+    s_first[e] = INT_MAX;
+    s_last[e] = -1;
+  }
+  for (int sl = tid; sl < S; sl += kRouteThreads) {
+    s_s2e[sl] = a.L.s2e[sl];
+    s_key[sl] = (long long)a.L.key[sl];
+  }
+  if (tid == 0) s_nevict = 0;
 
   // ---- router: one row per wavefront -------------------------------------
-  constexpr int EPL = kMaxExperts / 64;
-  const int epl = (E + 63) / 64;
   for (int m = wave; m < M; m += kRouteThreads / 64) {
-    const float* z = a.logits + (size_t)m * E;
-    uint64_t keys[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      int e = lane + 64 * i;
-      keys[i] = (i < epl && e < E) ? order_key(z[e], e) : 0ull;
-    }
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t loc = 0;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) loc = keys[i] > loc ? keys[i] : loc;
-      uint64_t best = wave_max_u64(loc);
-      int eb = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + 64 * i == eb) keys[i] = 0ull;
-      if (lane == j) my_e = eb;
-    }
+    int my_e;
+    float zj;
+    route_row<EPL>(a.logits + (size_t)m * E, E, k, lane, &my_e, &zj);
     // weights: softmax over the k chosen logits (limits for non-finite picks)
     const bool act = lane < k;
-    float zj = act ? z[my_e] : 0.0f;
+    if (!act) zj = 0.0f;
     const bool is_nan = zj != zj;
     const bool pinf = act && zj == INFINITY;
     const int npinf = __popcll(__ballot(pinf));
-    const float z0 = __shfl(zj, 0);
+    const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
     float w;
     if (npinf > 0) {
       w = pinf ? 1.0f / (float)npinf : 0.0f;
     } else if (z0 != z0 || z0 == -INFINITY) {
       w = 1.0f / (float)k;
     } else {
-      float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
-      float sum = wave_sum_f32(ex);
+      const float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
+      const float sum = wave_sum_f32(ex);
       w = ex / sum;
     }
     if (act) {
@@ -185,11 +294,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       a.W.pick_w[m * k + lane] = w;
     }
   }
-  for (int e = tid; e < E; e += kRouteThreads) {
-    s_first[e] = INT_MAX;
-    s_last[e] = -1;
-  }
-  if (tid == 0) s_nevict = 0;
   __syncthreads();
 
   // ---- unique experts in first-occurrence order ----------------------------
@@ -200,11 +304,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   __syncthreads();
   int U = 0;
   for (int base = 0; base < P; base += kRouteThreads) {
-    int p = base + tid;
-    int e = p < P ? s_pick[p] : 0;
-    bool f = p < P && s_first[e] == p;
+    const int p = base + tid;
+    const int e = p < P ? s_pick[p] : 0;
+    const bool f = p < P && s_first[e] == p;
     int tot;
-    int r = block_rank(f, s_wc, &tot);
+    const int r = block_rank(f, s_wc, &tot);
     if (f) {
       s_uexp[U + r] = e;
       s_uidx[e] = U + r;
@@ -219,51 +323,90 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   if (!bypass) {
     // ---- hit test against the slot map ------------------------------------
     for (int u = tid; u < U; u += kRouteThreads) {
-      int s = a.L.e2s[s_uexp[u]];
-      if (s < -1 || s >= S) {
+      int sl = s_e2s[s_uexp[u]];
+      if (sl < -1 || sl >= S) {
         atomicOr(a.L.error, 1u);
-        s = -1;
+        sl = -1;
       }
-      s_uslot[u] = s;
+      s_uslot[u] = sl;
     }
     __syncthreads();
     for (int base = 0; base < U; base += kRouteThreads) {
-      int u = base + tid;
-      bool ms = u < U && s_uslot[u] < 0;
+      const int u = base + tid;
+      const bool ms = u < U && s_uslot[u] < 0;
       int tot;
-      int r = block_rank(ms, s_wc, &tot);
+      const int r = block_rank(ms, s_wc, &tot);
       if (u < U) s_umiss[u] = ms ? nmiss + r : -1;
       nmiss += tot;
     }
     __syncthreads();
     if (nmiss > 0) {
-      // ---- victims: candidates ranked by (key, slot) -----------------------
-      for (int s = tid; s < S; s += kRouteThreads) s_ref[s] = 0;
+      // ---- victims: the nmiss least (key, slot) among slots not hit ---------
+      for (int sl = tid; sl < S; sl += kRouteThreads) s_ref[sl] = 0;
       __syncthreads();
       for (int u = tid; u < U; u += kRouteThreads)
         if (s_uslot[u] >= 0) s_ref[s_uslot[u]] = 1;
       __syncthreads();
-      for (int s = tid; s < S; s += kRouteThreads)
-        s_ckey[s] = s_ref[s] ? (long long)LLONG_MAX : (long long)a.L.key[s];
-      __syncthreads();
-      for (int s = tid; s < S; s += kRouteThreads) {
-        if (s_ref[s]) continue;
-        const long long ks = s_ckey[s];
-        int r = 0;
-        for (int s2 = 0; s2 < S; ++s2) {
-          long long k2 = s_ckey[s2];
-          r += (k2 < ks) || (k2 == ks && s2 < s);
+      if (nmiss <= 8) {
+        // a few misses: repeated block minimum over packed (key + 2, slot);
+        // keys are >= -1, so a candidate packs to >= 2^11 and ~0 means "none"
+        uint64_t ck[SPT];
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+          const int sl = tid + q * kRouteThreads;
+          ck[q] = (sl < S && !s_ref[sl]) ? (((uint64_t)(s_key[sl] + 2) << 11) | (uint64_t)sl) : ~0ull;
         }
-        if (r < nmiss) s_victim[r] = s;
+        for (int i = 0; i < nmiss; ++i) {
+          uint64_t loc = ~0ull;
+#pragma unroll
+          for (int q = 0; q < SPT; ++q) loc = ck[q] < loc ? ck[q] : loc;
+          const uint64_t wm = wave_reduce_u64<false>(loc);
+          if (lane == 0) s_wmin[wave] = wm;
+          __syncthreads();
+          uint64_t g = s_wmin[0];
+#pragma unroll
+          for (int w = 1; w < kRouteThreads / 64; ++w) g = s_wmin[w] < g ? s_wmin[w] : g;
+#pragma unroll
+          for (int q = 0; q < SPT; ++q)
+            if (ck[q] == g) ck[q] = ~0ull;
+          if (tid == 0) s_victim[i] = g == ~0ull ? -1 : (int)(g & 0x7FFull);
+          __syncthreads();
+        }
+      } else {
+        // many misses: rank every candidate by (key, slot)
+        for (int sl = tid; sl < S; sl += kRouteThreads) {
+          if (s_ref[sl]) s_key[sl] = (long long)LLONG_MAX;
+          s_victim[sl] = -1;
+        }
+        __syncthreads();
+        for (int sl = tid; sl < S; sl += kRouteThreads) {
+          if (s_ref[sl]) continue;
+          const long long ks = s_key[sl];
+          int r = 0;
+          for (int s2 = 0; s2 < S; ++s2) {
+            const long long k2 = s_key[s2];
+            r += (k2 < ks) || (k2 == ks && s2 < sl);
+          }
+          if (r < nmiss) s_victim[r] = sl;
+        }
       }
       __syncthreads();
       // ---- apply the misses: evict, remap, log, queue the fills ------------
       for (int u = tid; u < U; u += kRouteThreads) {
-        int i = s_umiss[u];
+        const int i = s_umiss[u];
         if (i < 0) continue;
-        int e = s_uexp[u];
-        int s = s_victim[i];
-        int old = a.L.s2e[s];
+        const int e = s_uexp[u];
+        const int sl = s_victim[i];
+        if (sl < 0 || sl >= S) {
+          // no victim (cannot happen while |U| <= S): read this expert from the
+          // backing store, leave the maps alone, and make the fill skip it
+          atomicOr(a.L.error, 4u);
+          s_uslot[u] = -1;
+          a.W.miss_src[i] = nullptr;
+          a.W.miss_dst[i] = nullptr;
+          continue;
+        }
+        int old = s_s2e[sl];
         if (old >= E) {
           atomicOr(a.L.error, 2u);
           old = -1;
@@ -272,56 +415,66 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
           a.L.e2s[old] = -1;
           atomicAdd(&s_nevict, 1);
         }
-        a.L.e2s[e] = s;
-        a.L.s2e[s] = e;
-        s_uslot[u] = s;
+        a.L.e2s[e] = sl;
+        a.L.s2e[sl] = e;
+        s_uslot[u] = sl;
         sc_event ev;
         ev.step = t;
         ev.expert = e;
-        ev.slot = s;
+        ev.slot = sl;
         ev.evicted = old;
         ev.reserved = 0;
         a.L.events[(ev_head + (uint64_t)i) % (uint64_t)a.L.ev_cap] = ev;
         a.W.miss_src[i] = a.L.backing + (size_t)e * B;
-        a.W.miss_dst[i] = a.L.slots + (size_t)s * B;
+        a.W.miss_dst[i] = a.L.slots + (size_t)sl * B;
       }
       __syncthreads();
     }
     // ---- stamp the clock, publish slot pointers ----------------------------
     for (int u = tid; u < U; u += kRouteThreads) {
-      int s = s_uslot[u];
-      a.L.key[s] = t * (int64_t)(kCachedRows * k) + (int64_t)s_last[s_uexp[u]];
-      a.W.uniq_ptr[u] = a.L.slots + (size_t)s * B;
+      const int sl = s_uslot[u];
+      if (sl < 0) {
+        a.W.uniq_ptr[u] = a.L.backing + (size_t)s_uexp[u] * B;
+        continue;
+      }
+      a.L.key[sl] = t * (int64_t)(kCachedRows * k) + (int64_t)s_last[s_uexp[u]];
+      a.W.uniq_ptr[u] = a.L.slots + (size_t)sl * B;
     }
   } else {
     for (int u = tid; u < U; u += kRouteThreads)
       a.W.uniq_ptr[u] = a.L.backing + (size_t)s_uexp[u] * B;
   }
-  for (int u = tid; u < U; u += kRouteThreads) {
-    int e = s_uexp[u];
-    a.W.uniq_expert[u] = e;
-    a.W.uniq_gs[2 * u] = a.L.gs[2 * e];
-    a.W.uniq_gs[2 * u + 1] = a.L.gs[2 * e + 1];
-    s_cnt[u] = 0;
-  }
-  __syncthreads();
+  for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_expert[u] = s_uexp[u];
 
   // ---- picks grouped by unique expert (CSR), ascending pick order ---------
-  for (int p = tid; p < P; p += kRouteThreads) {
-    int u = s_uidx[s_pick[p]];
-    atomicAdd(&s_cnt[u], 1);
-    a.W.pick_u[p] = u;
+  if (U == P) {
+    // every pick is its own unique expert, in pick order
+    for (int p = tid; p < P; p += kRouteThreads) {
+      a.W.pick_u[p] = p;
+      a.W.uniq_picks[p] = p;
+      a.W.uniq_off[p] = p;
+    }
+  } else {
+    int* s_cnt = s_first;   // free after the unique pass
+    int* s_off = s_umiss;   // free after the miss pass
+    __syncthreads();
+    for (int u = tid; u < U; u += kRouteThreads) s_cnt[u] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kRouteThreads) {
+      const int u = s_uidx[s_pick[p]];
+      atomicAdd(&s_cnt[u], 1);
+      a.W.pick_u[p] = u;
+    }
+    __syncthreads();
+    block_scan(s_cnt, s_off, U, s_wc);
+    for (int p = tid; p < P; p += kRouteThreads) {
+      const int e = s_pick[p];
+      int r = 0;
+      for (int q = 0; q < p; ++q) r += s_pick[q] == e;
+      a.W.uniq_picks[s_off[s_uidx[e]] + r] = p;
+    }
+    for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_off[u] = s_off[u];
   }
-  __syncthreads();
-  block_scan(s_cnt, s_off, U, s_wc);
-  for (int p = tid; p < P; p += kRouteThreads) {
-    const int e = s_pick[p];
-    int r = 0;
-    for (int q = 0; q < p; ++q) r += s_pick[q] == e;
-    a.W.uniq_picks[s_off[s_uidx[e]] + r] = p;
-  }
-  for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_off[u] = s_off[u];
-  __syncthreads();
 
   if (tid == 0) {
     a.W.uniq_off[U] = P;
@@ -329,20 +482,21 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     a.W.hdr[H_MISS] = nmiss;
     a.W.hdr[H_BYPASS] = bypass ? 1 : 0;
     a.W.hdr[H_ROWS] = M;
-    uint64_t* c = a.L.counters;
-    c[C_STEPS] += 1;
+    cnt[C_STEPS] += 1;
     if (bypass) {
-      c[C_BYPASS] += 1;
-      c[C_BYPASS_BYTES] += (uint64_t)U * (uint64_t)B;
+      cnt[C_BYPASS] += 1;
+      cnt[C_BYPASS_BYTES] += (uint64_t)U * (uint64_t)B;
     } else {
-      c[C_PICKS] += (uint64_t)P;
-      c[C_LOOKUPS] += (uint64_t)U;
-      c[C_HITS] += (uint64_t)(U - nmiss);
-      c[C_MISSES] += (uint64_t)nmiss;
-      c[C_EVICT] += (uint64_t)s_nevict;
-      c[C_FILLED] += (uint64_t)nmiss * (uint64_t)B;
+      cnt[C_PICKS] += (uint64_t)P;
+      cnt[C_LOOKUPS] += (uint64_t)U;
+      cnt[C_HITS] += (uint64_t)(U - nmiss);
+      cnt[C_MISSES] += (uint64_t)nmiss;
+      cnt[C_EVICT] += (uint64_t)s_nevict;
+      cnt[C_FILLED] += (uint64_t)nmiss * (uint64_t)B;
       *a.L.ev_head = ev_head + (uint64_t)nmiss;
     }
+#pragma unroll
+    for (int c = 0; c < C_N; ++c) a.L.counters[c] = cnt[c];
     *a.L.step = t + 1;
   }
 }
@@ -350,15 +504,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
-                        const float* logits, int M, hipStream_t st) {
+                        const float* logits, int M, hipStream_t st, KEvents ev) {
   RouteArgs a;
   a.sh = sh;
   a.L = L;
   a.W = W;
   a.logits = logits;
   a.M = M;
-  hipLaunchKernelGGL(k_route_remap, dim3(1), dim3(kRouteThreads), 0, st, a);
-  return hipGetLastError();
+  const int epl = (sh.E + 63) / 64;
+  const dim3 g(1), b(kRouteThreads);
+  if (epl <= 1) return sc_launch(k_route_remap<1>, g, b, st, ev, a);
+  if (epl <= 2) return sc_launch(k_route_remap<2>, g, b, st, ev, a);
+  if (epl <= 4) return sc_launch(k_route_remap<4>, g, b, st, ev, a);
+  if (epl <= 8) return sc_launch(k_route_remap<8>, g, b, st, ev, a);
+  return sc_launch(k_route_remap<16>, g, b, st, ev, a);
 }
 
 }  // namespace sc

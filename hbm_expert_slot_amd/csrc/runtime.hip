@@ -61,7 +61,7 @@ LayerOffsets layer_offsets(int E, int S, int cap) {
 }
 
 struct WsOffsets {
-  size_t hdr, pick_expert, pick_w, pick_u, uniq_expert, uniq_ptr, uniq_gs, uniq_off, uniq_picks,
+  size_t hdr, pick_expert, pick_w, pick_u, uniq_expert, uniq_ptr, uniq_off, uniq_picks,
       miss_src, miss_dst, h, part, end;
 };
 
@@ -74,7 +74,6 @@ WsOffsets ws_offsets(int Pmax, int H, int I) {
   o.pick_u = p; p = align_up(p + (size_t)Pmax * 4);
   o.uniq_expert = p; p = align_up(p + (size_t)Pmax * 4);
   o.uniq_ptr = p; p = align_up(p + (size_t)Pmax * 8);
-  o.uniq_gs = p; p = align_up(p + (size_t)Pmax * 8);
   o.uniq_off = p; p = align_up(p + (size_t)(Pmax + 1) * 4);
   o.uniq_picks = p; p = align_up(p + (size_t)Pmax * 4);
   o.miss_src = p; p = align_up(p + (size_t)Pmax * 8);
@@ -288,7 +287,6 @@ sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
   h->W.pick_u = reinterpret_cast<int32_t*>(ws + o.pick_u);
   h->W.uniq_expert = reinterpret_cast<int32_t*>(ws + o.uniq_expert);
   h->W.uniq_ptr = reinterpret_cast<const uint8_t**>(ws + o.uniq_ptr);
-  h->W.uniq_gs = reinterpret_cast<float*>(ws + o.uniq_gs);
   h->W.uniq_off = reinterpret_cast<int32_t*>(ws + o.uniq_off);
   h->W.uniq_picks = reinterpret_cast<int32_t*>(ws + o.uniq_picks);
   h->W.miss_src = reinterpret_cast<const uint8_t**>(ws + o.miss_src);
@@ -372,20 +370,19 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
   hipStream_t s = static_cast<hipStream_t>(stream);
   LayerDev L = layer_dev(h, layer);
   hipError_t e = hipSuccess;
-  auto rec = [&](int i) {
-    if (events && e == hipSuccess) e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  auto kev = [&](int i) {
+    KEvents k;
+    if (events) {
+      k.start = static_cast<hipEvent_t>(events[2 * i]);
+      k.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+    }
+    return k;
   };
-  rec(0);
-  if (e == hipSuccess) e = launch_route(h->sh, L, h->W, d_logits, M, s);
-  rec(1);
-  if (e == hipSuccess) e = launch_fill(h->sh, h->W, s);
-  rec(2);
-  if (e == hipSuccess) e = launch_gateup(h->sh, h->W, d_x, M, s);
-  rec(3);
-  if (e == hipSuccess) e = launch_down(h->sh, h->W, M, s);
-  rec(4);
-  if (e == hipSuccess) e = launch_combine(h->sh, h->W, d_y, M, s);
-  rec(5);
+  e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
+  if (e == hipSuccess) e = launch_fill(h->sh, h->W, s, kev(1));
+  if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, s, kev(2));
+  if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, s, kev(3));
+  if (e == hipSuccess) e = launch_combine(h->sh, h->W, d_y, M, s, kev(4));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   h->last_stream = s;
   h->stepped = true;

@@ -154,12 +154,14 @@ SC_API sc_status slotcache_preload(sc_handle* h, int32_t layer);
 SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits,
                            const uint16_t* d_x, int32_t M, float* d_y, void* stream);
 
-/* Phases of one step, for per-kernel timing. */
-#define SC_N_EVENTS 6
-/* moe_layer_decode plus hipEventRecord of events[i] (hipEvent_t passed as
- * void*) before the routing kernel (0), after routing+remap (1), after the miss
- * fill (2), after gate/up (3), after down (4) and after the combine (5).
- * events == NULL is moe_layer_decode. */
+/* Kernels of one step, for per-kernel timing: routing+remap, miss fill,
+ * gate/up, down, combine. */
+#define SC_N_KERNELS 5
+#define SC_N_EVENTS (2 * SC_N_KERNELS)
+/* moe_layer_decode with per-kernel timing: events[2i] and events[2i+1]
+ * (hipEvent_t passed as void*, created by the caller) are stamped at the start
+ * and the end of kernel i's execution (hipExtLaunchKernelGGL).  events == NULL
+ * is moe_layer_decode. */
 SC_API sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits,
                               const uint16_t* d_x, int32_t M, float* d_y, void* stream,
                               void* const* events);

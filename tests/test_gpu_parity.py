@@ -305,3 +305,29 @@ def test_glm_drafted_rounds_and_prefill_bypass():
     log("GLM drafted worst rel L2 %.3g; stats %s" % (worst, st))
     assert st["bypass_steps"] == 2
     sc.close()
+
+
+def test_timed_entry_point_matches_the_plain_one():
+    """moe_layer_decode_ev (per-kernel start/stop events) computes the same step."""
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("timed entry point vs plain: tiny, 24 steps")
+    a, b = make_cache(cfg), make_cache(cfg)
+    logits, _ = routing_trace(cfg, 0)
+    for t in range(24):
+        z = torch.from_numpy(logits[t, :1]).cuda()
+        x = torch.from_numpy(activations(cfg, 0, t, 1).view(np.int16)).cuda()
+        ya = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
+        yb = torch.empty_like(ya)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+        for ev in evs:
+            ev.record()
+        a.decode(0, z, x, ya)
+        b.decode(0, z, x, yb, events=evs)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb), t
+        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(5))
+    for u, v in zip(a.read_state(0), b.read_state(0)):
+        assert np.array_equal(u, v)
+    a.close()
+    b.close()
