@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="back-to-back steps (Infinity Cache may serve repeats)")
     ap.add_argument("--cpu-baseline-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-rows", default="",
+                    help="comma-separated M values: all-hit GLM layer (every expert resident), drafted rows; "
+                         "prints one JSON line per M instead of the headline line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (counter calibration)")
     return ap.parse_args()
@@ -108,6 +111,64 @@ def cpu_baseline(cfg, logits, x_rows, start, nsteps):
     }
 
 
+def sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace):
+    """All-hit GLM layer (S = E, preloaded) at several M, drafted rows; graph replay, cache swept."""
+    import dataclasses
+    base = CONFIGS["glm_draft"]
+    Ms = [int(v) for v in a.sweep_rows.split(",")]
+    Mmax = max(Ms)
+    dev = torch.device("cuda:0")
+    sc = SlotCache(1, base.hidden, base.inter, base.n_experts, base.top_k, base.n_experts, Mmax)
+    expert_blobs(base, 0, out=sc.backing(0))
+    sc.set_global_scales(0, global_scales(base, 0, "unit"))
+    sc.preload(0)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    gstream = torch.cuda.Stream(dev)
+    K = a.steps
+    for M in Ms:
+        cfg = dataclasses.replace(base, rows=M, schedule="fixed", drafted=M <= 16)
+        logits, _ = routing_trace(cfg, 0, steps=K)
+        xs = np.stack([activations(cfg, 0, t, M) for t in range(K)])
+        d_l = torch.from_numpy(logits).to(dev)
+        d_x = torch.from_numpy(xs.view(np.int16)).to(dev)
+        d_y = torch.empty((K, M, cfg.hidden), dtype=torch.float32, device=dev)
+        for t in range(min(K, 4)):
+            sc.decode(0, d_l[t], d_x[t], d_y[t])
+        torch.cuda.synchronize()
+        st0 = sc.stats(0)
+        graphs = []
+        for with_steps in (True, False):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(gstream):
+                g.capture_begin()
+                for t in range(K):
+                    sink.copy_(flush.amax())
+                    if with_steps:
+                        sc.decode(0, d_l[t], d_x[t], d_y[t], stream=gstream)
+                g.capture_end()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        times = []
+        for g in graphs:
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        st1 = sc.stats(0)
+        us = (times[0] - times[1]) * 1e3 / K
+        uniq = (st1["lookups"] - st0["lookups"]) / max(1, st1["steps"] - st0["steps"])
+        byts = uniq * sc.blob_bytes
+        print(json.dumps({"sweep": "all-hit GLM layer, drafted rows", "M": M, "us_per_step": round(us, 2),
+                          "unique_experts_per_step": round(uniq, 2), "weight_GBs": round(byts / (us * 1e-6) / 1e9, 1)}), flush=True)
+    sc.close()
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -127,6 +188,9 @@ def main():
     from hbm_expert_slot_amd.cache import SlotCache
     from synth import CONFIGS, activations, expert_blobs, global_scales, routing_trace
 
+    if a.sweep_rows:
+        sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace)
+        return
     cfg = CONFIGS[a.config]
     if cfg.rows != 1 or cfg.n_layers != 1:
         print("bench.py times the single-layer M=1 workloads (tiny, glm)", file=sys.stderr)
