@@ -183,7 +183,13 @@ struct XRed {
 // time with the next R steps' code and scale loads issued before the current
 // ones are consumed (register double buffering), so every wavefront always has
 // two groups of loads in flight.
-template <int K, int MR, int R, bool GATEUP, bool STRIDED>
+//
+// SINGLE: a one-row step.  Its k picks are k distinct experts, so U = k and
+// pick u is unique expert u (the remap's CSR lists are the identity): the
+// kernel takes U from the launch instead of the header and skips the CSR
+// lookups, so a wavefront's first weight loads wait for one pointer load only
+// and its activation loads for none.
+template <int K, int MR, int R, bool GATEUP, bool STRIDED, bool SINGLE = false>
 struct Gemv {
   using G = Geo<K>;
   static constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
@@ -265,7 +271,8 @@ struct Gemv {
   }
 
   __device__ static __forceinline__ void run(const GemvArgs& a) {
-    const int U = a.hdr[H_UNIQUE];
+    static_assert(!SINGLE || MR == 1, "one-row steps have one pick per expert");
+    const int U = SINGLE ? a.k : a.hdr[H_UNIQUE];
     const int lane = threadIdx.x & 63;
     const int seg = lane % LPR, rsub = lane / LPR;
     const int nwaves = gridDim.x * (kGemvThreads / 64);
@@ -292,7 +299,7 @@ struct Gemv {
       if (n <= 0) continue;
       const uint8_t* blob = a.uniq_ptr[u];
       const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
-      const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
+      const int off0 = SINGLE ? u : a.uniq_off[u], off1 = SINGLE ? u + 1 : a.uniq_off[u + 1];
       const uint8_t* code_base = blob + a.code_off + seg * 16;
       const uint8_t* scale_base = blob + a.scale_off + seg * 2;
       for (int c0 = off0; c0 < off1; c0 += MR) {
@@ -303,14 +310,14 @@ struct Gemv {
         uint32_t opw[MR][NSEG][OPW];
 #pragma unroll
         for (int mi = 0; mi < MR; ++mi) {
-          pk[mi] = mi < nc ? a.uniq_picks[c0 + mi] : 0;
+          pk[mi] = SINGLE ? c0 : (mi < nc ? a.uniq_picks[c0 + mi] : 0);
 #pragma unroll
           for (int c = 0; c < NSEG; ++c) {
             const int e0 = c * 2048 + seg * 32;
             const uint4* src;
             if (GATEUP)
               src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.operand) +
-                                                   (size_t)(pk[mi] / a.k) * K + e0);
+                                                   (size_t)(SINGLE ? 0 : pk[mi] / a.k) * K + e0);
             else
               src = reinterpret_cast<const uint4*>(static_cast<const float*>(a.operand) +
                                                    (size_t)pk[mi] * K + e0);
@@ -340,9 +347,9 @@ struct Gemv {
   }
 };
 
-template <int K, int MR, int R, bool GATEUP, bool STRIDED>
+template <int K, int MR, int R, bool GATEUP, bool STRIDED, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
-  Gemv<K, MR, R, GATEUP, STRIDED>::run(a);
+  Gemv<K, MR, R, GATEUP, STRIDED, SINGLE>::run(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -543,22 +550,25 @@ constexpr int stage_rows() {
   return want < lim ? want : lim;
 }
 
-template <int K, int MR, bool GATEUP>
+template <int K, int MR, bool GATEUP, bool SINGLE>
 GemvFn gemv_fn() {
-  return k_gemv<K, MR, stage_rows<K, MR, GATEUP>(), GATEUP, false>;
+  return k_gemv<K, MR, stage_rows<K, MR, GATEUP>(), GATEUP, false, SINGLE>;
 }
 
+// MR = 0 selects the one-row variant (one pick per expert, U = k).
 template <bool GATEUP, int MR>
 GemvFn pick_gemv(int K) {
+  constexpr int mr = MR == 0 ? 1 : MR;
+  constexpr bool single = MR == 0;
   switch (K) {
-    case 128: return GATEUP ? nullptr : gemv_fn<128, MR, GATEUP>();
-    case 256: return gemv_fn<256, MR, GATEUP>();
-    case 512: return gemv_fn<512, MR, GATEUP>();
-    case 1024: return gemv_fn<1024, MR, GATEUP>();
-    case 2048: return gemv_fn<2048, MR, GATEUP>();
-    case 4096: return gemv_fn<4096, MR, GATEUP>();
-    case 6144: return gemv_fn<6144, MR, GATEUP>();
-    case 8192: return gemv_fn<8192, MR, GATEUP>();
+    case 128: return GATEUP ? nullptr : gemv_fn<128, mr, GATEUP, single>();
+    case 256: return gemv_fn<256, mr, GATEUP, single>();
+    case 512: return gemv_fn<512, mr, GATEUP, single>();
+    case 1024: return gemv_fn<1024, mr, GATEUP, single>();
+    case 2048: return gemv_fn<2048, mr, GATEUP, single>();
+    case 4096: return gemv_fn<4096, mr, GATEUP, single>();
+    case 6144: return gemv_fn<6144, mr, GATEUP, single>();
+    case 8192: return gemv_fn<8192, mr, GATEUP, single>();
     default: return nullptr;
   }
 }
@@ -620,7 +630,7 @@ int mfma_blocks(long maxu, int rows) {
 }  // namespace
 
 bool gemv_supported(int K, bool gateup) {
-  return gateup ? pick_gemv<true, 1>(K) != nullptr : pick_gemv<false, 1>(K) != nullptr;
+  return gateup ? pick_gemv<true, 0>(K) != nullptr : pick_gemv<false, 0>(K) != nullptr;
 }
 
 hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev) {
@@ -656,7 +666,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
     return sc_launch(fn, dim3(mfma_blocks(maxu, sh.I)), dim3(kGemvThreads), st, ev, a);
   }
   const int mr = mr_for(M);
-  GemvFn fn = mr == 1 ? pick_gemv<true, 1>(sh.H) : pick_gemv<true, 2>(sh.H);
+  GemvFn fn = M == 1 ? pick_gemv<true, 0>(sh.H) : pick_gemv<true, 2>(sh.H);
   if (!fn) return hipErrorInvalidValue;
   const long stages = maxu * (sh.I / rows_per_wave(sh.H)) / stage_rows_rt(sh.H, mr, true);
   return sc_launch(fn, dim3(gemv_blocks(stages, kGateupBlocks)), dim3(kGemvThreads), st, ev, a);
@@ -679,7 +689,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
     return sc_launch(fn, dim3(mfma_blocks(maxu, sh.H)), dim3(kGemvThreads), st, ev, a);
   }
   const int mr = mr_for(M);
-  GemvFn fn = mr == 1 ? pick_gemv<false, 1>(sh.I) : pick_gemv<false, 2>(sh.I);
+  GemvFn fn = M == 1 ? pick_gemv<false, 0>(sh.I) : pick_gemv<false, 2>(sh.I);
   if (!fn) return hipErrorInvalidValue;
   const long stages = maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, mr, false);
   return sc_launch(fn, dim3(gemv_blocks(stages, kDownBlocks)), dim3(kGemvThreads), st, ev, a);
