@@ -28,7 +28,7 @@ METRIC = "µs per MoE layer-step (M=1) + achieved HBM GB/s vs peak; LRU hit rate
 HBM_PEAK_GBS = 8000.0
 PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16, per direction
 PHASES = ("route_remap", "fill", "gateup", "down", "combine")
-KERNEL_NAMES = {"gateup": "k_gemv<6144, 1, 1, true, false>", "down": "k_gemv<2048, 1, 8, false, false>"}
+KERNEL_NAMES = {"gateup": "k_gemv<6144, 1, 1, true, false, true>", "down": "k_gemv<2048, 1, 8, false, false, true>"}
 
 
 def parse():
@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--sweep-rows", default="",
                     help="comma-separated M values: all-hit GLM layer (every expert resident), drafted rows; "
                          "prints one JSON line per M instead of the headline line")
+    ap.add_argument("--dump-steps", default="",
+                    help="write the timed steps' all-hit indices and gate/up event durations to this JSON file")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "STEPS_JSON"),
+                    help="only summarize a rocprofv3 kernel trace of this bench: gate/up durations over the "
+                         "all-hit timed launches listed by --dump-steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (counter calibration)")
     return ap.parse_args()
@@ -169,8 +174,35 @@ def sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_s
     sc.close()
 
 
+def trace_summary(trace_csv, steps_json):
+    """Average rocprofv3 duration of the gate/up kernel over the all-hit timed launches.
+
+    The bench launches the gate/up kernel once per step: `warmup` eager steps,
+    then the `timed` eager steps (the ones --dump-steps lists), then graph
+    replays; launch j of the timed pass is dispatch warmup + j in the trace."""
+    import csv
+    st = json.load(open(steps_json))
+    rows = [r for r in csv.DictReader(open(trace_csv)) if "k_gemv<6144, 1, 1, true" in r.get("Kernel_Name", "")]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    W, K = st["warmup"], st["timed"]
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    timed = dur[W:W + K]
+    hit = [timed[i] for i in st["all_hit_timed_steps"]]
+    ev = st["gateup_us_events"]
+    sp = st["gateup_us_spans"]
+    print(json.dumps({"spans_avg_us_all_hit": round(float(np.mean([sp[i] for i in st["all_hit_timed_steps"]])), 3),
+                      "gateup_launches_in_trace": len(dur), "timed_launches": len(timed),
+                      "all_hit_launches": len(hit),
+                      "rocprof_avg_us_all_hit": round(float(np.mean(hit)), 3),
+                      "events_avg_us_all_hit": round(float(np.mean([ev[i] for i in st["all_hit_timed_steps"]])), 3),
+                      "rocprof_avg_us_all_launches": round(float(np.mean(dur)), 3)}))
+
+
 def main():
     a = parse()
+    if a.trace_summary:
+        trace_summary(*a.trace_summary)
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X "
               "(no collectives); --gpus %d is not supported" % a.gpus, file=sys.stderr)
@@ -219,21 +251,24 @@ def main():
     st0 = sc.stats(0)
     ev0 = sc.read_events(0)[1]
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(PHASES))] for _ in range(K)]
     for row in evs:          # torch creates the HIP event on first record
         for ev in row:
             ev.record(stream)
     torch.cuda.synchronize()
+    spans = []
     wall0 = time.perf_counter()
     for i in range(K):
         if not a.no_flush:
             flush_sink.copy_(flush.amax())     # read-only sweep: evicts clean, writes nothing back
         sc.decode(0, d_logits[W + i], d_x[W + i], d_y[W + i], stream=stream, events=evs[i])
+        spans.append(sc.kernel_spans())       # synchronizes: one step at a time
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    span_us = {p: np.array([spans[i][j] for i in range(K)]) for j, p in enumerate(PHASES)}
 
     # step: start of the routing kernel to the end of the combine; kernels: own start/end stamps
-    step_us = np.array([evs[i][0].elapsed_time(evs[i][9]) * 1e3 for i in range(K)])
+    step_us = np.array([evs[i][0].elapsed_time(evs[i][-1]) * 1e3 for i in range(K)])
     phase_us = {p: np.array([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) * 1e3 for i in range(K)])
                 for j, p in enumerate(PHASES)}
     st1 = sc.stats(0)
@@ -245,7 +280,9 @@ def main():
     hits = st1["hits"] - st0["hits"]
     misses = st1["misses"] - st0["misses"]
     filled = st1["bytes_filled"] - st0["bytes_filled"]
-    fill_us = phase_us["fill"]
+    gu_us = span_us["gateup"]
+    hit_idx = [i for i in range(K) if step_ids[i] not in miss_steps]
+    fill_us = span_us["fill"]
     fill_time_miss = float(np.sum([fill_us[i] for i in range(K) if step_ids[i] in miss_steps]))
 
     # ---- graph replay: the same K steps captured in one HIP graph -------------
@@ -292,8 +329,15 @@ def main():
     U = k  # M=1: the k picks are distinct experts
     gateup_bytes = U * (2 * I * H // 2 + 2 * I * H // 16) + H * 2 + k * I * 4
     down_bytes = U * (H * I // 2 + H * I // 16) + k * I * 4 + k * H * 4
-    gu = float(np.mean(phase_us["gateup"]))
-    dn = float(np.mean(phase_us["down"]))
+    # roofline: the gate/up kernel on the timed steps without a miss (a miss step's slot was just
+    # written by the fill, so part of it can come from the Infinity Cache)
+    gu = float(np.mean(gu_us[hit_idx])) if hit_idx else float("nan")
+    dn = float(np.mean(span_us["down"][hit_idx])) if hit_idx else float("nan")
+    if a.dump_steps:
+        with open(a.dump_steps, "w") as f:
+            json.dump({"warmup": W, "timed": K, "all_hit_timed_steps": hit_idx,
+                       "gateup_us_spans": [float(v) for v in gu_us],
+                       "gateup_us_events": [float(v) for v in phase_us["gateup"]]}, f)
     src_hash = source_hash()
     traffic = pmc_traffic("gateup_glm_m1", src_hash)
     result = {
@@ -315,8 +359,9 @@ def main():
             "infinity_cache": "flushed between steps (512 MiB read sweep, not timed)" if not a.no_flush
                               else "not flushed (back-to-back steps; repeats may hit the 256 MiB cache)",
             "timing": "value: one HIP-graph replay of the K steps (each after the cache sweep) minus a replay of "
-                      "the K sweeps alone, divided by K; eager step_us/kernels_us: an eager pass over the same steps "
-                      "with HIP events stamped at each kernel's own start and end",
+                      "the K sweeps alone, divided by K; eager pass over the same steps, one step at a time: step_us "
+                      "from HIP events (routing kernel start to combine end), kernels_us from the kernels' own "
+                      "start/end stamps on the device wall clock (slotcache_read_kernel_spans)",
         },
         "graph": {"us_per_step": graph_us, "replay_ms": steps_ms, "sweeps_ms": sweeps_ms,
                   "hit_rate": g_hits / g_lookups if g_lookups else None},
@@ -324,7 +369,8 @@ def main():
                     "p50": float(np.percentile(step_us, 50)), "p90": float(np.percentile(step_us, 90)),
                     "all_hit_mean": float(np.mean(allhit)) if allhit.size else None,
                     "all_hit_steps": int(allhit.size)},
-        "kernels_us": {p: float(np.mean(v)) for p, v in phase_us.items()},
+        "kernels_us": {p: float(np.mean(v)) for p, v in span_us.items()},
+        "kernels_us_all_hit_steps": {p: float(np.mean(v[hit_idx])) for p, v in span_us.items()} if hit_idx else None,
         "lru": {"hit_rate": hits / lookups if lookups else None, "misses_per_step": misses / K,
                 "lookups": lookups, "hits": hits, "misses": misses},
         "roofline": {
@@ -333,6 +379,7 @@ def main():
             "frac": round(gateup_bytes / (gu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": gu,
+            "launches": "gate/up kernel on the %d all-hit timed steps" % len(hit_idx),
         },
         "down_gemv": {"kernel": KERNEL_NAMES["down"], "achieved_GBs": round(down_bytes / (dn * 1e-6) / 1e9, 1),
                       "avg_launch_us": dn, "algorithmic_bytes_per_launch": down_bytes},

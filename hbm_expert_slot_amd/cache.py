@@ -66,6 +66,10 @@ class SlotCache:
                                   ctypes.cast(arr, ctypes.c_void_p))
 
     # ---- readback --------------------------------------------------------------
+    def kernel_spans(self):
+        """Execution spans (us) of the kernels of the last timed step (decode with events)."""
+        return B.slotcache_read_kernel_spans(self.h)
+
     def stats(self, layer):
         st = B.slotcache_stats(self.h, layer)
         return {name: int(getattr(st, name)) for name, _ in B.sc_stats._fields_ if name != "reserved"}

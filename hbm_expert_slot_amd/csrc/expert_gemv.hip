@@ -51,6 +51,7 @@ struct GemvArgs {
   int up_row0;           // gate/up: first up row (I)
   int64_t code_off;      // offset of the code rows inside a blob
   int64_t scale_off;     // offset of the scale rows inside a blob
+  uint64_t* span;        // execution stamps of a timed step, else null
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
@@ -349,7 +350,9 @@ struct Gemv {
 
 template <int K, int MR, int R, bool GATEUP, bool STRIDED, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+  span_start(a.span);
   Gemv<K, MR, R, GATEUP, STRIDED, SINGLE>::run(a);
+  span_end(a.span);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +489,9 @@ struct GemvMfma {
 
 template <int K, bool GATEUP, int RT>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvArgs a) {
+  span_start(a.span);
   GemvMfma<K, GATEUP, RT>::run(a);
+  span_end(a.span);
 }
 
 // Copies the step's missed blobs (host-mapped pinned memory -> HBM slots).
@@ -495,7 +500,8 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvArgs a) {
 // Entries whose destination is null (a miss the remap could not place) are
 // skipped.
 __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t* const* src,
-                                               uint8_t* const* dst, long n16) {
+                                               uint8_t* const* dst, long n16, uint64_t* span) {
+  span_start(span);
   const long total = (long)hdr[H_MISS] * n16;
   const long stride = (long)gridDim.x * blockDim.x;
   long o = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -516,28 +522,32 @@ __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t*
     const long i = o / n16;
     if (dst[i]) *reinterpret_cast<uint4*>(dst[i] + (o - i * n16) * 16) = ld16(src[i] + (o - i * n16) * 16);
   }
+  span_end(span);
 }
 
 // y[m][r] = sum over j = 0..k-1 of w[m][j] * part[m*k + j][r], in rank order.
 __global__ __launch_bounds__(256) void k_combine(const float* part, const float* w, float* y,
-                                                  int M, int k, int H) {
+                                                  int M, int k, int H, uint64_t* span) {
+  span_start(span);
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)M * H) return;
-  const int m = (int)(idx / H), r = (int)(idx - (long)m * H);
-  const float* pp = part + (size_t)m * k * H + r;
-  const float* wm = w + m * k;
-  float acc = 0.0f;
-  int j = 0;
-  // eight partial loads in flight at a time; the sum keeps rank order
-  for (; j + 8 <= k; j += 8) {
-    float v[8];
+  if (idx < (long)M * H) {
+    const int m = (int)(idx / H), r = (int)(idx - (long)m * H);
+    const float* pp = part + (size_t)m * k * H + r;
+    const float* wm = w + m * k;
+    float acc = 0.0f;
+    int j = 0;
+    // eight partial loads in flight at a time; the sum keeps rank order
+    for (; j + 8 <= k; j += 8) {
+      float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = pp[(size_t)(j + i) * H];
+      for (int i = 0; i < 8; ++i) v[i] = pp[(size_t)(j + i) * H];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(wm[j + i], v[i], acc);
+      for (int i = 0; i < 8; ++i) acc = fmaf(wm[j + i], v[i], acc);
+    }
+    for (; j < k; ++j) acc = fmaf(wm[j], pp[(size_t)j * H], acc);
+    y[idx] = acc;
   }
-  for (; j < k; ++j) acc = fmaf(wm[j], pp[(size_t)j * H], acc);
-  y[idx] = acc;
+  span_end(span);
 }
 
 typedef void (*GemvFn)(GemvArgs);
@@ -635,7 +645,7 @@ bool gemv_supported(int K, bool gateup) {
 
 hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev) {
   return sc_launch(k_fill, dim3(kFillBlocks), dim3(256), st, ev, (const int32_t*)W.hdr,
-                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16));
+                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16), ev.span);
 }
 
 static GemvArgs base_args(const Workspace& W, const float* gs) {
@@ -646,6 +656,7 @@ static GemvArgs base_args(const Workspace& W, const float* gs) {
   a.gs = gs;
   a.uniq_off = W.uniq_off;
   a.uniq_picks = W.uniq_picks;
+  a.span = nullptr;
   return a;
 }
 
@@ -659,6 +670,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.up_row0 = sh.I;
   a.code_off = 0;
   a.scale_off = sh.off_w13s;
+  a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<true>(sh.H);
@@ -682,6 +694,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   a.up_row0 = 0;
   a.code_off = sh.off_w2c;
   a.scale_off = sh.off_w2s;
+  a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<false>(sh.I);
@@ -699,7 +712,7 @@ hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, 
                           KEvents ev) {
   const long n = (long)M * sh.H;
   return sc_launch(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), st, ev, (const float*)W.part,
-                   (const float*)W.pick_w, y, M, sh.k, sh.H);
+                   (const float*)W.pick_w, y, M, sh.k, sh.H, ev.span);
 }
 
 }  // namespace sc

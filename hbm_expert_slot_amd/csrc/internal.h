@@ -83,10 +83,29 @@ inline Shape make_shape(int H, int I, int E, int k) {
 
 // Optional start/stop events of one launch (both null: a plain launch).  With
 // events the kernel is launched through hipExtLaunchKernelGGL, which stamps
-// the events at the kernel's own start and end.
+// the events at the kernel's own start and end.  `span`, when set, receives
+// the launch's execution stamps (see span_start / span_end).
 struct KEvents {
   hipEvent_t start = nullptr, stop = nullptr;
+  uint64_t* span = nullptr;
 };
+
+// Execution stamps of one launch, in ticks of the device's constant wall clock
+// (s_memrealtime): block b writes its start to span[b * kSpanSlots] and each
+// of its wavefronts w its end, after its memory operations have completed, to
+// span[b * kSpanSlots + 1 + w].  Kernels of a timed step write them; the host
+// keeps the stamps not older than the step's routing kernel start.
+constexpr int kSpanSlots = 5;   // start + one end per wavefront (at most 4 per block)
+__device__ __forceinline__ void span_start(uint64_t* span) {
+  if (span && threadIdx.x == 0) span[(size_t)blockIdx.x * kSpanSlots] = (uint64_t)wall_clock64();
+}
+__device__ __forceinline__ void span_end(uint64_t* span) {
+  if (span) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's stores are done
+    if ((threadIdx.x & 63) == 0)
+      span[(size_t)blockIdx.x * kSpanSlots + 1 + (threadIdx.x >> 6)] = (uint64_t)wall_clock64();
+  }
+}
 
 template <typename F, typename... Args>
 inline hipError_t sc_launch(F kernel, dim3 grid, dim3 block, hipStream_t st, KEvents ev, Args... args) {

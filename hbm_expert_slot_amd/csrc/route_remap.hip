@@ -170,6 +170,7 @@ struct RouteArgs {
   Workspace W;
   const float* logits;
   int M;
+  uint64_t* span;
 };
 
 // Router for one row on one wavefront: lane l holds the keys of experts
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   __shared__ unsigned long long s_wmin[kRouteThreads / 64];
   __shared__ int s_nevict;
 
+  span_start(a.span);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.sh.E, k = a.sh.k, M = a.M, S = a.L.S;
@@ -499,6 +501,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     for (int c = 0; c < C_N; ++c) a.L.counters[c] = cnt[c];
     *a.L.step = t + 1;
   }
+  span_end(a.span);
 }
 
 }  // namespace
@@ -511,6 +514,7 @@ hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
   a.W = W;
   a.logits = logits;
   a.M = M;
+  a.span = ev.span;
   const int epl = (sh.E + 63) / 64;
   const dim3 g(1), b(kRouteThreads);
   if (epl <= 1) return sc_launch(k_route_remap<1>, g, b, st, ev, a);

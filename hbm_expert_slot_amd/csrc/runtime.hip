@@ -62,10 +62,17 @@ LayerOffsets layer_offsets(int E, int S, int cap) {
 
 struct WsOffsets {
   size_t hdr, pick_expert, pick_w, pick_u, uniq_expert, uniq_ptr, uniq_off, uniq_picks,
-      miss_src, miss_dst, h, part, end;
+      miss_src, miss_dst, h, part, span, end;
 };
 
-WsOffsets ws_offsets(int Pmax, int H, int I) {
+// Blocks a launch of the step can have: the GEMV grids are capped at 1024; the
+// combine has one block per 256 outputs.
+int span_blocks(int Pmax_rows, int H) {
+  const long comb = ((long)Pmax_rows * H + 255) / 256;
+  return (int)(comb > 1024 ? comb : 1024);
+}
+
+WsOffsets ws_offsets(int Pmax, int H, int I, int max_rows) {
   WsOffsets o;
   size_t p = 0;
   o.hdr = p; p = align_up(p + H_WORDS * 4);
@@ -80,6 +87,7 @@ WsOffsets ws_offsets(int Pmax, int H, int I) {
   o.miss_dst = p; p = align_up(p + (size_t)Pmax * 8);
   o.h = p; p = align_up(p + (size_t)Pmax * I * 4);
   o.part = p; p = align_up(p + (size_t)Pmax * H * 4);
+  o.span = p; p = align_up(p + (size_t)SC_N_KERNELS * span_blocks(max_rows, H) * kSpanSlots * 8);
   o.end = p;
   return o;
 }
@@ -137,6 +145,10 @@ struct sc_handle {
   std::vector<void*> bank_dev;
   hipStream_t last_stream;
   bool stepped;
+  bool timed;                       // the last step was a timed one (spans written)
+  uint64_t* d_span;                 // [SC_N_KERNELS][span_cap][kSpanSlots]
+  int span_cap;
+  int clock_khz;                    // wall clock rate of the span stamps
 };
 
 namespace {
@@ -166,7 +178,7 @@ Sizes compute_sizes(const sc_config* c) {
   state += align_up((size_t)c->n_banks * c->n_experts * 2 * sizeof(float));
   z.pool = pool;
   z.state = state;
-  z.wo = ws_offsets(c->max_rows * c->top_k, c->hidden, c->inter);
+  z.wo = ws_offsets(c->max_rows * c->top_k, c->hidden, c->inter, c->max_rows);
   z.ws = z.wo.end;
   z.bank = (size_t)c->n_experts * (size_t)sh.blob;
   return z;
@@ -293,6 +305,16 @@ sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
   h->W.miss_dst = reinterpret_cast<uint8_t**>(ws + o.miss_dst);
   h->W.h = reinterpret_cast<float*>(ws + o.h);
   h->W.part = reinterpret_cast<float*>(ws + o.part);
+  h->d_span = reinterpret_cast<uint64_t*>(ws + o.span);
+  h->span_cap = span_blocks(cfg->max_rows, cfg->hidden);
+  h->timed = false;
+  h->clock_khz = 0;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&h->clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+      (void)hipGetLastError();
+  }
 
   // Cold state: every slot empty, keys -1, counters and rings zero, gs = 1.
   std::vector<uint8_t> img(z.state, 0);
@@ -375,6 +397,7 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
     if (events) {
       k.start = static_cast<hipEvent_t>(events[2 * i]);
       k.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
+      k.span = h->d_span + (size_t)i * h->span_cap * kSpanSlots;
     }
     return k;
   };
@@ -386,12 +409,39 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   h->last_stream = s;
   h->stepped = true;
+  h->timed = events != nullptr;
   return SC_OK;
 }
 
 sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
                            int32_t M, float* d_y, void* stream) {
   return moe_layer_decode_ev(h, layer, d_logits, d_x, M, d_y, stream, nullptr);
+}
+
+sc_status slotcache_read_kernel_spans(sc_handle* h, double* us_out) {
+  if (!h) return fail(SC_E_ARG, "handle is NULL");
+  if (!us_out) return fail(SC_E_ARG, "us_out is NULL");
+  if (!h->timed) return fail(SC_E_STATE, "the last step was not run through moe_layer_decode_ev");
+  if (h->clock_khz <= 0) return fail(SC_E_UNSUPPORTED, "device wall clock rate unknown");
+  sc_status st = sync_last(h);
+  if (st != SC_OK) return st;
+  const size_t per = (size_t)h->span_cap * kSpanSlots;
+  std::vector<uint64_t> s((size_t)SC_N_KERNELS * per);
+  hipError_t e = hipMemcpy(s.data(), h->d_span, s.size() * 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (spans)");
+  // stamps older than this step's routing kernel start are left over from earlier steps
+  const uint64_t t0 = s[0];
+  for (int i = 0; i < SC_N_KERNELS; ++i) {
+    uint64_t lo = UINT64_MAX, hi = 0;
+    for (int b = 0; b < h->span_cap; ++b) {
+      const uint64_t* r = &s[i * per + (size_t)b * kSpanSlots];
+      if (r[0] >= t0 && r[0] < lo) lo = r[0];
+      for (int w = 1; w < kSpanSlots; ++w)
+        if (r[w] >= t0 && r[w] > hi) hi = r[w];
+    }
+    us_out[i] = (lo == UINT64_MAX || hi < lo) ? 0.0 : (double)(hi - lo) * 1000.0 / (double)h->clock_khz;
+  }
+  return SC_OK;
 }
 
 sc_status slotcache_stats(sc_handle* h, int32_t layer, sc_stats* out) {

@@ -166,6 +166,15 @@ SC_API sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d
                               const uint16_t* d_x, int32_t M, float* d_y, void* stream,
                               void* const* events);
 
+/* Execution spans of the kernels of the most recent step run through
+ * moe_layer_decode_ev, in microseconds: us_out[i] (i < SC_N_KERNELS) is the
+ * time from kernel i's first block start to its last wavefront end, read from
+ * stamps the kernels write with the device's constant wall clock.  (The stop
+ * events of hipExtLaunchKernelGGL land a few microseconds after a kernel's
+ * end, which matters for kernels of tens of microseconds.)  Synchronizes the
+ * stream of the last step.  SC_E_STATE if that step was not a timed one. */
+SC_API sc_status slotcache_read_kernel_spans(sc_handle* h, double* us_out);
+
 /* Counters of `layer`.  Synchronizes the stream of the last step. */
 SC_API sc_status slotcache_stats(sc_handle* h, int32_t layer, sc_stats* out);
 

@@ -308,8 +308,9 @@ def test_glm_drafted_rounds_and_prefill_bypass():
 
 
 def test_timed_entry_point_matches_the_plain_one():
-    """moe_layer_decode_ev (per-kernel start/stop events) computes the same step."""
+    """moe_layer_decode_ev (per-kernel start/stop events and execution stamps) computes the same step."""
     torch = torch_cuda()
+    from hbm_expert_slot_amd import binding as B
     cfg = CONFIGS["tiny"]
     log("timed entry point vs plain: tiny, 24 steps")
     a, b = make_cache(cfg), make_cache(cfg)
@@ -319,15 +320,66 @@ def test_timed_entry_point_matches_the_plain_one():
         x = torch.from_numpy(activations(cfg, 0, t, 1).view(np.int16)).cuda()
         ya = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
         yb = torch.empty_like(ya)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(B.SC_N_EVENTS)]
         for ev in evs:
             ev.record()
         a.decode(0, z, x, ya)
         b.decode(0, z, x, yb, events=evs)
         torch.cuda.synchronize()
         assert torch.equal(ya, yb), t
-        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(5))
+        ev_ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(B.SC_N_KERNELS)]
+        assert all(v >= 0 for v in ev_ms)
+        # the kernels' own start/end stamps: positive, and inside the event brackets
+        spans = b.kernel_spans()
+        assert all(0 < s_us <= 1e3 * e_ms + 1.0 for s_us, e_ms in zip(spans, ev_ms)), (spans, ev_ms)
+    with pytest.raises(B.SlotCacheError):
+        a.kernel_spans()          # a's steps were not timed
     for u, v in zip(a.read_state(0), b.read_state(0)):
         assert np.array_equal(u, v)
     a.close()
     b.close()
+
+
+def _check_slots_hold_their_experts(sc, layer=0):
+    """Every occupied slot holds its expert's blob byte for byte (single-layer pools)."""
+    e2s, s2e, key, step = sc.read_state(layer)
+    pool = sc.pool[: sc.slots[layer] * sc.blob_bytes].cpu().numpy().reshape(sc.slots[layer], sc.blob_bytes)
+    back = sc.backing(layer % sc.n_banks)
+    filled = 0
+    for s, e in enumerate(s2e):
+        if e >= 0:
+            assert np.array_equal(pool[s], back[e]), (s, e)
+            filled += 1
+    return filled
+
+
+@pytest.mark.parametrize("shape", ["tiny", "glm48"])
+def test_misses_fill_their_slots_exactly(shape):
+    """Misses are filled by the gate/up launch (read-through of the gate/up rows,
+    copy blocks for the down rows): after a churning mix of one-row, multi-row
+    (experts with several picks) and matrix-core steps every occupied slot must
+    equal its expert's blob."""
+    cfg = CONFIGS["tiny"]
+    if shape == "glm48":
+        g = CONFIGS["glm"]
+        cfg = WorkloadConfig("glm48", g.hidden, g.inter, 48, g.top_k, 30, rows=16, steps=40, seed=g.seed)
+    log("slot contents after churn: %s, M in {1, 2, 3, 4, 8, 12, 16}" % shape)
+    sc = make_cache(cfg, max_rows=16)
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(9)
+    Ms = [1, 4, 2, 16, 1, 3, 12, 8, 1, 4]
+    E = cfg.n_experts
+    zs = []
+    for t in range(30):
+        z = rng.standard_normal((16, E)).astype(np.float32)
+        z[:, : max(2, cfg.top_k // 2)] += 2.0      # shared favourites: several picks per expert
+        zs.append(z)
+    sample = None if shape == "tiny" else {0, 1, 6, 9}     # M = 1, 4, 12, 4 (fp64 oracle cost at GLM shapes)
+    worst = _run_trace(cfg, sc, orc, 30, lambda t: Ms[t % len(Ms)], lambda t: zs[t], y_steps=sample,
+                       state_every=5)
+    st = sc.stats(0)
+    n = _check_slots_hold_their_experts(sc)
+    log("%s: %d occupied slots verified; misses %d, bypass %d, worst rel L2 %.3g" % (shape, n, st["misses"],
+                                                                                   st["bypass_steps"], worst))
+    assert st["misses"] > 0 and n > 0
+    sc.close()
