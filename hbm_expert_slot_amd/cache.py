@@ -12,7 +12,7 @@ from . import binding as B
 
 class SlotCache:
     def __init__(self, n_layers, hidden, inter, n_experts, top_k, slots, max_rows,
-                 n_banks=1, event_capacity=0, device="cuda"):
+                 n_banks=1, event_capacity=0, device="cuda", batch_invariant=False):
         import torch
 
         self.torch = torch
@@ -22,7 +22,8 @@ class SlotCache:
         self.n_layers, self.hidden, self.inter = n_layers, hidden, inter
         self.n_experts, self.top_k, self.max_rows, self.n_banks = n_experts, top_k, max_rows, n_banks
         self.cfg = B.make_config(n_layers, hidden, inter, n_experts, top_k, self.slots, max_rows,
-                                 n_banks, event_capacity)
+                                 n_banks, event_capacity,
+                                 flags=B.SC_FLAG_BATCH_INVARIANT if batch_invariant else 0)
         self.sizes = B.slotcache_query_sizes(self.cfg)
         self.blob_bytes = self.sizes.blob_bytes
         self.device = torch.device(device)

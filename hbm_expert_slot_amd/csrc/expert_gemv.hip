@@ -661,7 +661,7 @@ static GemvArgs base_args(const Workspace& W, const float* gs) {
 }
 
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
-                         hipStream_t st, KEvents ev) {
+                         bool mfma, hipStream_t st, KEvents ev) {
   GemvArgs a = base_args(W, gs);
   a.operand = x;
   a.out = W.h;
@@ -672,7 +672,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.scale_off = sh.off_w13s;
   a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  if (M >= kMfmaMinRows) {
+  if (mfma && M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<true>(sh.H);
     if (!fn) return hipErrorInvalidValue;
     return sc_launch(fn, dim3(mfma_blocks(maxu, sh.I)), dim3(kGemvThreads), st, ev, a);
@@ -684,7 +684,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   return sc_launch(fn, dim3(gemv_blocks(stages, kGateupBlocks)), dim3(kGemvThreads), st, ev, a);
 }
 
-hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, hipStream_t st,
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, hipStream_t st,
                        KEvents ev) {
   GemvArgs a = base_args(W, gs);
   a.operand = W.h;
@@ -696,7 +696,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   a.scale_off = sh.off_w2s;
   a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  if (M >= kMfmaMinRows) {
+  if (mfma && M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<false>(sh.I);
     if (!fn) return hipErrorInvalidValue;
     return sc_launch(fn, dim3(mfma_blocks(maxu, sh.H)), dim3(kGemvThreads), st, ev, a);

@@ -123,9 +123,10 @@ bool gemv_supported(int K, bool gateup);
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
                         const float* logits, int M, hipStream_t st, KEvents ev);
 hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev);
+// mfma: the matrix-core kernels may serve M >= 12 (off: the streaming kernels for every M).
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
-                         hipStream_t st, KEvents ev);
-hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, hipStream_t st,
+                         bool mfma, hipStream_t st, KEvents ev);
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, hipStream_t st,
                        KEvents ev);
 hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,
                           KEvents ev);

@@ -112,7 +112,7 @@ sc_status check_config(const sc_config* c) {
     return fail(SC_E_ARG, "max_rows * top_k must be <= %d", kMaxPicks);
   if (c->n_banks < 1 || c->n_banks > c->n_layers) return fail(SC_E_ARG, "n_banks must be in [1, n_layers]");
   if (c->event_capacity < 0) return fail(SC_E_ARG, "event_capacity must be >= 0");
-  if (c->flags != 0) return fail(SC_E_ARG, "flags must be 0");
+  if (c->flags & ~(uint32_t)SC_FLAG_BATCH_INVARIANT) return fail(SC_E_ARG, "unknown flags 0x%x", c->flags);
   if (!c->slots_per_layer) return fail(SC_E_ARG, "slots_per_layer is NULL");
   for (int l = 0; l < c->n_layers; ++l) {
     int S = c->slots_per_layer[l];
@@ -403,8 +403,9 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
   };
   e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
   if (e == hipSuccess) e = launch_fill(h->sh, h->W, s, kev(1));
-  if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, s, kev(2));
-  if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, s, kev(3));
+  const bool mfma = !(h->cfg.flags & SC_FLAG_BATCH_INVARIANT);
+  if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, s, kev(2));
+  if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, s, kev(3));
   if (e == hipSuccess) e = launch_combine(h->sh, h->W, d_y, M, s, kev(4));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   h->last_stream = s;

@@ -83,8 +83,16 @@ typedef struct {
   int32_t max_rows;               /* largest M the caller will pass, 1..256 */
   int32_t n_banks;                /* host backing banks, 1..n_layers; layer l reads bank l % n_banks */
   int32_t event_capacity;         /* per-layer miss-event ring, records (0 = 4096) */
-  uint32_t flags;                 /* reserved, must be 0 */
+  uint32_t flags;                 /* 0 or SC_FLAG_BATCH_INVARIANT */
 } sc_config;
+
+/* Every row of a step computes the bits it would compute alone, as a one-row
+ * step: the streaming FP4 kernels run for every M (their per-row reduction
+ * order does not depend on how many rows share an expert) and the matrix-core
+ * kernels, whose rounding differs, are not used.  Drafted and verify rows then
+ * never change a row's output (the exact-decoding rule on the page "TensorFold
+ * GLM-5.3 explained").  Costs speed at M >= 12. */
+#define SC_FLAG_BATCH_INVARIANT 1u
 
 typedef struct {
   size_t blob_bytes;              /* B_e */

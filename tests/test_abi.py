@@ -60,7 +60,7 @@ def test_sizes_for_the_glm_layer():
     (dict(hidden=6000), B.SC_E_ARG),
     (dict(hidden=3072), B.SC_E_UNSUPPORTED),
     (dict(inter=64), B.SC_E_UNSUPPORTED),
-    (dict(flags=1), B.SC_E_ARG),
+    (dict(flags=2), B.SC_E_ARG),
 ])
 def test_invalid_configs_are_rejected(kw, code):
     with pytest.raises(B.SlotCacheError) as ei:

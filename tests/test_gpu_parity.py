@@ -383,3 +383,58 @@ def test_misses_fill_their_slots_exactly(shape):
                                                                                    st["bypass_steps"], worst))
     assert st["misses"] > 0 and n > 0
     sc.close()
+
+
+def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True):
+    """Max number of rows whose output differs (bitwise) from the same row run as a one-row step."""
+    torch = torch_cuda()
+    rng = np.random.default_rng(seed)
+    E, H = cfg.n_experts, cfg.hidden
+    bad = {}
+    for t, M in enumerate(Ms):
+        z = rng.standard_normal((M, E)).astype(np.float32)
+        if drafted:                   # later rows share picks with row 0 (draft / verify rounds)
+            top = np.argsort(-z[0])[:cfg.top_k]
+            for m in range(1, M):
+                z[m, rng.choice(top, min(3, len(top)), replace=False)] += 20.0
+        x = activations(cfg, 0, 1000 + t, M)
+        zd = torch.from_numpy(z).cuda()
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+        sc_multi.decode(0, zd, xd, y)
+        ym = y.cpu().numpy()
+        n = 0
+        for m in range(M):
+            y1 = torch.empty((1, H), dtype=torch.float32, device="cuda")
+            sc_single.decode(0, zd[m:m + 1].contiguous(), xd[m:m + 1].contiguous(), y1)
+            n += int(not np.array_equal(ym[m], y1.cpu().numpy()[0]))
+        bad[M] = max(bad.get(M, 0), n)
+    return bad
+
+
+@pytest.mark.parametrize("shape", ["tiny", "glm32"])
+def test_batch_invariant_rows(shape):
+    """SC_FLAG_BATCH_INVARIANT: every row of an M-row step (drafted rows sharing
+    picks, M up to 16, and a prefill-sized bypass step) is bit-equal to the
+    same row decoded alone.  Without the flag the streaming kernels (M < 12)
+    are invariant too; the matrix-core kernels (M >= 12) need not be."""
+    cfg = CONFIGS["tiny"]
+    if shape == "glm32":
+        g = CONFIGS["glm"]
+        cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 32, rows=24, steps=1, seed=g.seed)
+    log("batch invariance: %s" % shape)
+    E = cfg.n_experts
+    inv = make_cache(cfg, n_layers=1, slots=[E], max_rows=24, batch_invariant=True)
+    dflt = make_cache(cfg, n_layers=1, slots=[E], max_rows=24)
+    one = make_cache(cfg, n_layers=1, slots=[E], max_rows=1)
+    for sc in (inv, dflt, one):
+        sc.preload(0)
+    Ms = [2, 3, 4, 8, 11, 12, 16, 24]
+    bad_inv = _rows_vs_single(cfg, inv, one, Ms, seed=3)
+    bad_dflt = _rows_vs_single(cfg, dflt, one, [M for M in Ms if M < 12], seed=3)
+    log("rows differing from their one-row result: invariant %s; default (M < 12) %s" % (bad_inv, bad_dflt))
+    assert all(v == 0 for v in bad_inv.values()), bad_inv
+    assert all(v == 0 for v in bad_dflt.values()), bad_dflt
+    assert inv.stats(0)["bypass_steps"] == 1      # M = 24 > 16
+    for sc in (inv, dflt, one):
+        sc.close()
