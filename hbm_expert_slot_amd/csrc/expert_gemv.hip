@@ -645,7 +645,8 @@ bool gemv_supported(int K, bool gateup) {
 
 hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev) {
   return sc_launch(k_fill, dim3(kFillBlocks), dim3(256), st, ev, (const int32_t*)W.hdr,
-                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16), ev.span);
+                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16),
+                   ev.span_for(kFillBlocks));
 }
 
 static GemvArgs base_args(const Workspace& W, const float* gs) {
@@ -670,18 +671,21 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.up_row0 = sh.I;
   a.code_off = 0;
   a.scale_off = sh.off_w13s;
-  a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (mfma && M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<true>(sh.H);
     if (!fn) return hipErrorInvalidValue;
-    return sc_launch(fn, dim3(mfma_blocks(maxu, sh.I)), dim3(kGemvThreads), st, ev, a);
+    const int blocks = mfma_blocks(maxu, sh.I);
+    a.span = ev.span_for(blocks);
+    return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
   const int mr = mr_for(M);
   GemvFn fn = M == 1 ? pick_gemv<true, 0>(sh.H) : pick_gemv<true, 2>(sh.H);
   if (!fn) return hipErrorInvalidValue;
   const long stages = maxu * (sh.I / rows_per_wave(sh.H)) / stage_rows_rt(sh.H, mr, true);
-  return sc_launch(fn, dim3(gemv_blocks(stages, kGateupBlocks)), dim3(kGemvThreads), st, ev, a);
+  const int blocks = gemv_blocks(stages, kGateupBlocks);
+  a.span = ev.span_for(blocks);
+  return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
 }
 
 hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, hipStream_t st,
@@ -694,25 +698,29 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   a.up_row0 = 0;
   a.code_off = sh.off_w2c;
   a.scale_off = sh.off_w2s;
-  a.span = ev.span;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (mfma && M >= kMfmaMinRows) {
     GemvFn fn = pick_mfma<false>(sh.I);
     if (!fn) return hipErrorInvalidValue;
-    return sc_launch(fn, dim3(mfma_blocks(maxu, sh.H)), dim3(kGemvThreads), st, ev, a);
+    const int blocks = mfma_blocks(maxu, sh.H);
+    a.span = ev.span_for(blocks);
+    return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
   const int mr = mr_for(M);
   GemvFn fn = M == 1 ? pick_gemv<false, 0>(sh.I) : pick_gemv<false, 2>(sh.I);
   if (!fn) return hipErrorInvalidValue;
   const long stages = maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, mr, false);
-  return sc_launch(fn, dim3(gemv_blocks(stages, kDownBlocks)), dim3(kGemvThreads), st, ev, a);
+  const int blocks = gemv_blocks(stages, kDownBlocks);
+  a.span = ev.span_for(blocks);
+  return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
 }
 
 hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,
                           KEvents ev) {
   const long n = (long)M * sh.H;
-  return sc_launch(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), st, ev, (const float*)W.part,
-                   (const float*)W.pick_w, y, M, sh.k, sh.H, ev.span);
+  const long blocks = (n + 255) / 256;
+  return sc_launch(k_combine, dim3((unsigned)blocks), dim3(256), st, ev, (const float*)W.part,
+                   (const float*)W.pick_w, y, M, sh.k, sh.H, ev.span_for(blocks));
 }
 
 }  // namespace sc

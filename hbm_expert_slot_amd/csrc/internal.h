@@ -88,6 +88,9 @@ inline Shape make_shape(int H, int I, int E, int k) {
 struct KEvents {
   hipEvent_t start = nullptr, stop = nullptr;
   uint64_t* span = nullptr;
+  int span_blocks = 0;       // blocks the span region holds
+  // the stamps region for a launch of `blocks` blocks (null if it would not fit)
+  uint64_t* span_for(long blocks) const { return blocks <= span_blocks ? span : nullptr; }
 };
 
 // Execution stamps of one launch, in ticks of the device's constant wall clock

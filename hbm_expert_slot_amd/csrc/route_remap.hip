@@ -514,7 +514,7 @@ hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
   a.W = W;
   a.logits = logits;
   a.M = M;
-  a.span = ev.span;
+  a.span = ev.span_for(1);
   const int epl = (sh.E + 63) / 64;
   const dim3 g(1), b(kRouteThreads);
   if (epl <= 1) return sc_launch(k_route_remap<1>, g, b, st, ev, a);

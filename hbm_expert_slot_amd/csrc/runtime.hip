@@ -65,11 +65,12 @@ struct WsOffsets {
       miss_src, miss_dst, h, part, span, end;
 };
 
-// Blocks a launch of the step can have: the GEMV grids are capped at 1024; the
-// combine has one block per 256 outputs.
+// Blocks of a launch whose execution stamps are kept: the GEMV grids are
+// capped at 1024 (2048 leaves room), the combine has one block per 256
+// outputs.  A larger launch runs without stamps.
 int span_blocks(int Pmax_rows, int H) {
   const long comb = ((long)Pmax_rows * H + 255) / 256;
-  return (int)(comb > 1024 ? comb : 1024);
+  return (int)(comb > 2048 ? comb : 2048);
 }
 
 WsOffsets ws_offsets(int Pmax, int H, int I, int max_rows) {
@@ -398,6 +399,7 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
       k.start = static_cast<hipEvent_t>(events[2 * i]);
       k.stop = static_cast<hipEvent_t>(events[2 * i + 1]);
       k.span = h->d_span + (size_t)i * h->span_cap * kSpanSlots;
+      k.span_blocks = h->span_cap;
     }
     return k;
   };
