@@ -26,7 +26,8 @@ EXPORTED = (
     "slotcache_query_sizes", "slotcache_init", "slotcache_backing", "slotcache_set_global_scales",
     "slotcache_preload", "moe_layer_decode", "moe_layer_decode_ev", "slotcache_stats",
     "slotcache_read_state", "slotcache_write_state", "slotcache_read_events",
-    "slotcache_read_routing", "slotcache_read_kernel_spans", "slotcache_last_error", "slotcache_destroy",
+    "slotcache_read_routing", "slotcache_read_kernel_spans", "slotcache_pin", "slotcache_last_error",
+    "slotcache_destroy",
 )
 
 
@@ -90,6 +91,7 @@ def lib():
             "slotcache_read_events": [P, i32, P, sz, ctypes.POINTER(sz), ctypes.POINTER(ctypes.c_uint64)],
             "slotcache_read_routing": [P, P, P, ctypes.POINTER(i32), ctypes.POINTER(i32)],
             "slotcache_read_kernel_spans": [P, ctypes.POINTER(ctypes.c_double)],
+            "slotcache_pin": [P, i32, P, i32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -176,6 +178,10 @@ def slotcache_read_routing(h, ids_ptr, w_ptr):
     M, byp = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().slotcache_read_routing(h, ids_ptr, w_ptr, ctypes.byref(M), ctypes.byref(byp)))
     return M.value, byp.value
+
+
+def slotcache_pin(h, layer, experts_ptr, n):
+    _check(lib().slotcache_pin(h, layer, experts_ptr, n))
 
 
 def slotcache_read_kernel_spans(h):

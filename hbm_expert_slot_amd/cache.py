@@ -49,6 +49,11 @@ class SlotCache:
     def preload(self, layer):
         B.slotcache_preload(self.h, layer)
 
+    def pin(self, layer, experts):
+        """Pin `experts` to the first len(experts) slots of `layer` (hybrid policy)."""
+        arr = np.ascontiguousarray(experts, dtype=np.int32)
+        B.slotcache_pin(self.h, layer, arr.ctypes.data if arr.size else None, int(arr.size))
+
     # ---- the step ------------------------------------------------------------
     def decode(self, layer, logits, x, y, stream=None, events=None):
         """logits fp32 [M, E], x bf16 bits (int16/uint16/bfloat16) [M, H], y fp32 [M, H]; all on device."""

@@ -43,6 +43,7 @@ struct LayerDev {
   const float* gs;         // [E][2] (w13, w2)
   int32_t S;
   int32_t ev_cap;
+  int32_t P;               // pinned slots [0, P): fixed experts, never victims
 };
 
 // Per-call scratch shared by all layers of a handle.

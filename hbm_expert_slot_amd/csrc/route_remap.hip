@@ -14,8 +14,13 @@
 // so they are per step):
 //   P  = the M*k picks in (row, rank) order, p = 0..M*k-1
 //   U  = unique experts of P in first-occurrence order; hits = resident ones
-//   bypass when M > 16 or |U| > S: the cache is untouched, blobs are read
-//          from the backing store, the step counter still advances
+//   bypass when M > 16 or |U| - (pinned hits) > S - P (P pinned slots; |U| > S
+//          without pins): the cache is untouched, the step counter still
+//          advances, resident experts are read from their slots and the
+//          others from the backing store (the pages' bypass reads
+//          non-resident experts: page "GB300 GLM 5.3 Testing", section on
+//          sizing the context window)
+//   pinned slots [0, P) hold fixed experts and are never victims
 //   candidates = slots not holding a hit, ascending (key, slot); empty slots
 //          have key -1; the i-th miss (first-occurrence order) takes the i-th
 //   key[slot(e)] = t * (16 * k) + last position of e in P, for every e in U
@@ -319,29 +324,33 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   }
   __syncthreads();
 
-  const bool bypass = (M > kCachedRows) || (U > S);
   const int64_t B = a.sh.blob;
-  int nmiss = 0;
+  const int Pn = a.L.P;
+  // ---- residency against the slot map (bypass steps use it too) -----------
+  for (int u = tid; u < U; u += kRouteThreads) {
+    int sl = s_e2s[s_uexp[u]];
+    if (sl < -1 || sl >= S) {
+      atomicOr(a.L.error, 1u);
+      sl = -1;
+    }
+    s_uslot[u] = sl;
+  }
+  __syncthreads();
+  int nmiss = 0, npin = 0;
+  for (int base = 0; base < U; base += kRouteThreads) {
+    const int u = base + tid;
+    const bool ms = u < U && s_uslot[u] < 0;
+    const bool pn = u < U && s_uslot[u] >= 0 && s_uslot[u] < Pn;
+    int tot, tot_pin;
+    const int r = block_rank(ms, s_wc, &tot);
+    (void)block_rank(pn, s_wc, &tot_pin);
+    if (u < U) s_umiss[u] = ms ? nmiss + r : -1;
+    nmiss += tot;
+    npin += tot_pin;
+  }
+  __syncthreads();
+  const bool bypass = (M > kCachedRows) || (U - npin > S - Pn);
   if (!bypass) {
-    // ---- hit test against the slot map ------------------------------------
-    for (int u = tid; u < U; u += kRouteThreads) {
-      int sl = s_e2s[s_uexp[u]];
-      if (sl < -1 || sl >= S) {
-        atomicOr(a.L.error, 1u);
-        sl = -1;
-      }
-      s_uslot[u] = sl;
-    }
-    __syncthreads();
-    for (int base = 0; base < U; base += kRouteThreads) {
-      const int u = base + tid;
-      const bool ms = u < U && s_uslot[u] < 0;
-      int tot;
-      const int r = block_rank(ms, s_wc, &tot);
-      if (u < U) s_umiss[u] = ms ? nmiss + r : -1;
-      nmiss += tot;
-    }
-    __syncthreads();
     if (nmiss > 0) {
       // ---- victims: the nmiss least (key, slot) among slots not hit ---------
       for (int sl = tid; sl < S; sl += kRouteThreads) s_ref[sl] = 0;
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
           const int sl = tid + q * kRouteThreads;
-          ck[q] = (sl < S && !s_ref[sl]) ? (((uint64_t)(s_key[sl] + 2) << 11) | (uint64_t)sl) : ~0ull;
+          ck[q] = (sl >= Pn && sl < S && !s_ref[sl]) ? (((uint64_t)(s_key[sl] + 2) << 11) | (uint64_t)sl) : ~0ull;
         }
         for (int i = 0; i < nmiss; ++i) {
           uint64_t loc = ~0ull;
@@ -377,12 +386,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       } else {
         // many misses: rank every candidate by (key, slot)
         for (int sl = tid; sl < S; sl += kRouteThreads) {
-          if (s_ref[sl]) s_key[sl] = (long long)LLONG_MAX;
+          if (s_ref[sl] || sl < Pn) s_key[sl] = (long long)LLONG_MAX;
           s_victim[sl] = -1;
         }
         __syncthreads();
         for (int sl = tid; sl < S; sl += kRouteThreads) {
-          if (s_ref[sl]) continue;
+          if (s_ref[sl] || sl < Pn) continue;
           const long long ks = s_key[sl];
           int r = 0;
           for (int s2 = 0; s2 < S; ++s2) {
@@ -443,8 +452,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       a.W.uniq_ptr[u] = a.L.slots + (size_t)sl * B;
     }
   } else {
-    for (int u = tid; u < U; u += kRouteThreads)
-      a.W.uniq_ptr[u] = a.L.backing + (size_t)s_uexp[u] * B;
+    // bypass: resident experts from their slots, the others from the backing store
+    for (int u = tid; u < U; u += kRouteThreads) {
+      const int sl = s_uslot[u];
+      a.W.uniq_ptr[u] = sl >= 0 ? a.L.slots + (size_t)sl * B : a.L.backing + (size_t)s_uexp[u] * B;
+    }
   }
   for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_expert[u] = s_uexp[u];
 
@@ -481,13 +493,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   if (tid == 0) {
     a.W.uniq_off[U] = P;
     a.W.hdr[H_UNIQUE] = U;
-    a.W.hdr[H_MISS] = nmiss;
+    a.W.hdr[H_MISS] = bypass ? 0 : nmiss;     // a bypass step fills nothing
     a.W.hdr[H_BYPASS] = bypass ? 1 : 0;
     a.W.hdr[H_ROWS] = M;
     cnt[C_STEPS] += 1;
     if (bypass) {
       cnt[C_BYPASS] += 1;
-      cnt[C_BYPASS_BYTES] += (uint64_t)U * (uint64_t)B;
+      cnt[C_BYPASS_BYTES] += (uint64_t)nmiss * (uint64_t)B;   // its non-resident experts
     } else {
       cnt[C_PICKS] += (uint64_t)P;
       cnt[C_LOOKUPS] += (uint64_t)U;

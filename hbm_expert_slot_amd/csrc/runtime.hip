@@ -146,6 +146,7 @@ struct sc_handle {
   std::vector<void*> bank_dev;
   hipStream_t last_stream;
   bool stepped;
+  std::vector<std::vector<int32_t>> pins;   // per layer: experts pinned in slots 0..P-1
   bool timed;                       // the last step was a timed one (spans written)
   uint64_t* d_span;                 // [SC_N_KERNELS][span_cap][kSpanSlots]
   int span_cap;
@@ -203,6 +204,7 @@ LayerDev layer_dev(sc_handle* h, int l) {
   L.gs = reinterpret_cast<const float*>(h->d_state + h->gs_off) + (size_t)bank * h->sh.E * 2;
   L.S = h->S[l];
   L.ev_cap = h->ev_cap;
+  L.P = (int32_t)h->pins[l].size();
   return L;
 }
 
@@ -275,6 +277,7 @@ sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
   h->wo = z.wo;
   h->last_stream = nullptr;
   h->stepped = false;
+  h->pins.assign(cfg->n_layers, {});
   for (int b = 0; b < cfg->n_banks; ++b) {
     void* p = nullptr;
     hipError_t e = hipHostMalloc(&p, z.bank, hipHostMallocDefault);
@@ -381,7 +384,42 @@ sc_status slotcache_preload(sc_handle* h, int32_t layer) {
   int64_t step = 0;
   e = hipMemcpy(&step, L.step, 8, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (step)");
+  h->pins[layer].clear();
   return put_state(h, layer, e2s, s2e, key, step);
+}
+
+sc_status slotcache_pin(sc_handle* h, int32_t layer, const int32_t* h_experts, int32_t n) {
+  sc_status st = check_layer(h, layer);
+  if (st != SC_OK) return st;
+  const int S = h->S[layer], E = h->sh.E;
+  if (n < 0 || n > S) return fail(SC_E_ARG, "n=%d must be in [0, S=%d]", n, S);
+  if (n > 0 && !h_experts) return fail(SC_E_ARG, "experts is NULL");
+  std::vector<int32_t> pins(h_experts, h_experts + n);
+  std::vector<char> seen(E, 0);
+  for (int i = 0; i < n; ++i) {
+    if (pins[i] < 0 || pins[i] >= E) return fail(SC_E_ARG, "expert %d out of range", pins[i]);
+    if (seen[pins[i]]) return fail(SC_E_ARG, "expert %d pinned twice", pins[i]);
+    seen[pins[i]] = 1;
+  }
+  if ((st = sync_last(h)) != SC_OK) return st;
+  LayerDev L = layer_dev(h, layer);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipMemcpy(L.slots + (size_t)i * h->sh.blob, L.backing + (size_t)pins[i] * h->sh.blob,
+                             (size_t)h->sh.blob, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy (pin)");
+  }
+  std::vector<int32_t> e2s(E, -1), s2e(S, -1);
+  std::vector<int64_t> key(S, -1);
+  for (int i = 0; i < n; ++i) {
+    s2e[i] = pins[i];
+    e2s[pins[i]] = i;
+  }
+  int64_t step = 0;
+  hipError_t e = hipMemcpy(&step, L.step, 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy (step)");
+  if ((st = put_state(h, layer, e2s, s2e, key, step)) != SC_OK) return st;
+  h->pins[layer] = pins;
+  return SC_OK;
 }
 
 sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
@@ -507,6 +545,9 @@ sc_status slotcache_write_state(sc_handle* h, int32_t layer, const int32_t* h_e2
       return fail(SC_E_ARG, "s2e[%d]=%d is not the inverse of e2s", s, e);
     if (e < 0 && h_key[s] != -1) return fail(SC_E_ARG, "empty slot %d must have key -1", s);
   }
+  const std::vector<int32_t>& pins = h->pins[layer];
+  for (size_t s = 0; s < pins.size(); ++s)
+    if (h_s2e[s] != pins[s]) return fail(SC_E_ARG, "pinned slot %zu must keep expert %d", s, pins[s]);
   if ((st = sync_last(h)) != SC_OK) return st;
   LayerDev L = layer_dev(h, layer);
   for (int s = 0; s < S; ++s) {

@@ -146,17 +146,18 @@ SC_API sc_status slotcache_backing(sc_handle* h, int32_t bank, void** host_ptr, 
 SC_API sc_status slotcache_set_global_scales(sc_handle* h, int32_t bank, const float* h_gs);
 
 /* Warm start for `layer`: slot s <- expert s for s < S (copied from the
- * backing store), keys -1.  Synchronous.  With S == E this makes every
- * expert resident (the all-resident layer). */
+ * backing store), keys -1, no pinned slots.  Synchronous.  With S == E this
+ * makes every expert resident (the all-resident layer). */
 SC_API sc_status slotcache_preload(sc_handle* h, int32_t layer);
 
 /* One decode step of `layer` for M rows (1 <= M <= max_rows):
  *   d_logits fp32 [M][E], d_x bf16 bits [M][H], d_y fp32 [M][H] (written).
  * Router: per row the k largest logits (ties -> lower expert id, NaN below
  * -inf), weights = softmax over the k chosen logits.  Cached steps (M <= 16
- * and at most S unique experts) remap, fill misses and compute from the
- * slots; other steps leave the cache untouched and compute from the backing
- * store.  Asynchronous on `stream`, no host synchronisation and no
+ * and at most S unique experts, see slotcache_pin for pinned slots) remap,
+ * fill misses and compute from the slots; other steps (bypass) leave the cache
+ * untouched and compute resident experts from their slots and the others from
+ * the backing store.  Asynchronous on `stream`, no host synchronisation and no
  * allocation, so it can be captured into a HIP graph (fixed addresses and
  * shapes).  Argument errors return before anything is enqueued. */
 SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits,
@@ -173,6 +174,17 @@ SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_lo
 SC_API sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits,
                               const uint16_t* d_x, int32_t M, float* d_y, void* stream,
                               void* const* events);
+
+/* Pins experts of `layer` (hybrid policy: page "GB300 GLM 5.3 Testing",
+ * section "Expert allocation vs a cache", compares a static pin with LRU):
+ * slot i <- h_experts[i] for i < n (copied from the backing store), never a
+ * victim; LRU runs over the other S - n slots, which are emptied (keys -1).
+ * 0 <= n <= S distinct ids; n = 0 unpins.  The step counter and counters are
+ * kept.  With n pinned slots a step bypasses when its unique experts outside
+ * the pinned set exceed S - n (the rule |U| > S for n = 0); n = S is a static
+ * pin.  slotcache_preload clears the pins; slotcache_write_state requires the
+ * pinned slots to keep their experts.  Synchronous. */
+SC_API sc_status slotcache_pin(sc_handle* h, int32_t layer, const int32_t* h_experts, int32_t n);
 
 /* Execution spans of the kernels of the most recent step run through
  * moe_layer_decode_ev, in microseconds: us_out[i] (i < SC_N_KERNELS) is the

@@ -15,7 +15,16 @@ bookkeeping is per step, not per pick):
   * U = unique experts of P in first-occurrence order; hits H = resident ones;
     misses = U minus H, in first-occurrence order.
   * A step bypasses (state untouched, step counter still advances) when M > 16
-    or |U| > S.
+    or when its unique experts do not fit: |U| > S.  A bypass step reads only
+    its non-resident experts from the host store; resident ones are read from
+    their slots (page "GB300 GLM 5.3 Testing", section on sizing the context
+    window: the bypass path reads non-resident experts per chunk), so its host
+    bytes are (non-resident unique experts) * B_e.
+  * Pinned slots (the hybrid policy; page "GB300 GLM 5.3 Testing", section
+    "Expert allocation vs a cache", compares pins with LRU): the first P slots
+    hold a fixed expert each and are never victims; LRU runs over the other
+    S - P.  The fit rule becomes |U| - (pinned hits) > S - P, which for P = 0
+    is |U| > S.
   * Victim candidates = slots whose resident is not a hit, sorted by
     (key, slot id); empty slots carry key -1 and so come first, in slot order.
     The i-th miss takes the i-th candidate; a resident there is evicted.
@@ -64,16 +73,34 @@ class SlotState:
         self.e2s = [-1] * n_experts
         self.s2e = [-1] * n_slots
         self.key = [-1] * n_slots
+        self.P = 0                  # pinned slots [0, P)
         self.t = 0
         self.counters = Counters()
 
     def preload(self):
-        """Warm start: slot s holds expert s (s < S), all keys -1."""
+        """Warm start: slot s holds expert s (s < S), all keys -1, no pins."""
+        self.P = 0
         self.e2s = [-1] * self.E
         for s in range(self.S):
             self.s2e[s] = s
             self.e2s[s] = s
             self.key[s] = -1
+
+    def pin(self, experts):
+        """Slot i holds experts[i] for good (i < P = len(experts) <= S); the other
+        slots are emptied; all keys -1.  Counters and the step counter are kept."""
+        experts = [int(e) for e in experts]
+        if len(experts) > self.S or len(set(experts)) != len(experts):
+            raise ValueError("need at most S distinct experts")
+        if any(not 0 <= e < self.E for e in experts):
+            raise ValueError("expert id out of range")
+        self.P = len(experts)
+        self.e2s = [-1] * self.E
+        self.s2e = [-1] * self.S
+        self.key = [-1] * self.S
+        for s, e in enumerate(experts):
+            self.s2e[s] = e
+            self.e2s[e] = s
 
     def step(self, ids) -> StepRecord:
         ids = np.asarray(ids)
@@ -96,15 +123,17 @@ class SlotState:
         self.t += 1
         c = self.counters
         c.steps += 1
-        if M > BYPASS_ROWS or len(uniques) > self.S:
+        resident = [self.e2s[e] >= 0 for e in uniques]
+        pinned_hits = sum(1 for e in uniques if 0 <= self.e2s[e] < self.P)
+        if M > BYPASS_ROWS or len(uniques) - pinned_hits > self.S - self.P:
             c.bypass_steps += 1
-            c.bypass_bytes += len(uniques) * self.blob_bytes
+            c.bypass_bytes += (len(uniques) - sum(resident)) * self.blob_bytes
             return StepRecord(t, True, uniques, [False] * len(uniques), [], [-1] * len(uniques),
                               unique_of_pick)
-        hit = [self.e2s[e] >= 0 for e in uniques]
+        hit = resident
         hit_set = {e for e, h in zip(uniques, hit) if h}
         misses = [e for e, h in zip(uniques, hit) if not h]
-        cands = self._victim_order([s for s in range(self.S) if self.s2e[s] not in hit_set])
+        cands = self._victim_order([s for s in range(self.P, self.S) if self.s2e[s] not in hit_set])
         events = []
         for i, e in enumerate(misses):
             s = cands[i]

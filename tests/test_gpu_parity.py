@@ -438,3 +438,46 @@ def test_batch_invariant_rows(shape):
     assert inv.stats(0)["bypass_steps"] == 1      # M = 24 > 16
     for sc in (inv, dflt, one):
         sc.close()
+
+
+@pytest.mark.parametrize("shape", ["tiny", "glm32"])
+def test_pinned_slots_against_the_oracle(shape):
+    """Hybrid policy (slotcache_pin): a few experts pinned in the first slots, LRU
+    over the rest, under one-row, multi-row, matrix-core and bypass steps: every
+    event, the slot map, keys and counters (bypass host bytes included) match
+    the oracle; pinned slots keep their experts; slot bytes stay exact."""
+    cfg = CONFIGS["tiny"]
+    npin, Ms = 3, [1, 2, 1, 3, 4, 1, 8, 17, 1, 2]
+    if shape == "glm32":
+        g = CONFIGS["glm"]
+        cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 16, rows=17, steps=30, seed=g.seed)
+        npin, Ms = 6, [1, 1, 2, 12, 1, 4, 17, 1, 1, 3]
+    log("pinned slots vs oracle: %s, %d pinned of %d" % (shape, npin, cfg.slots))
+    E = cfg.n_experts
+    sc = make_cache(cfg, max_rows=17)
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(17)
+    zs = []
+    for t in range(30):
+        z = rng.standard_normal((17, E)).astype(np.float32)
+        z[:, : cfg.top_k] += 1.0           # a few favourites, pinned below
+        zs.append(z)
+    pins = list(range(npin))[::-1]          # pinned in reverse id order: slot i holds npin-1-i
+    sc.pin(0, pins)
+    orc.state.pin(pins)
+    sample = None if shape == "tiny" else {0, 3, 6}
+    worst = _run_trace(cfg, sc, orc, 30, lambda t: Ms[t % len(Ms)], lambda t: zs[t], y_steps=sample)
+    e2s, s2e, key, step = sc.read_state(0)
+    assert list(s2e[:npin]) == pins
+    st = sc.stats(0)
+    n = _check_slots_hold_their_experts(sc)
+    log("pinned %s: worst rel L2 %.3g, stats %s, %d slots verified" % (shape, worst, st, n))
+    assert st["bypass_steps"] > 0 and st["misses"] > 0
+    bad_s2e = np.array(s2e)
+    bad_s2e[[0, 1]] = bad_s2e[[1, 0]]
+    bad_e2s = np.array(e2s)
+    bad_e2s[bad_s2e[0]], bad_e2s[bad_s2e[1]] = 0, 1
+    from hbm_expert_slot_amd import binding as B
+    with pytest.raises(B.SlotCacheError):
+        sc.write_state(0, bad_e2s, bad_s2e, key, step)      # pinned slots must keep their experts
+    sc.close()

@@ -17,13 +17,18 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden", "lru_hand_trace.json")
 
 
 class MoveToFront:
-    """Recency list from least to most recent; empty slots are used lowest id first."""
+    """Recency list from least to most recent; empty slots are used lowest id first.
+    Pinned experts sit in the first slots, outside the recency list."""
 
-    def __init__(self, E, S, preload=False):
+    def __init__(self, E, S, preload=False, pins=()):
         self.E, self.S = E, S
         self.slot_of = {}
         self.expert_in = [-1] * S
-        self.recency = []          # experts, LRU first
+        self.recency = []          # unpinned experts, LRU first
+        self.pinned = list(pins)
+        for s, e in enumerate(self.pinned):
+            self.slot_of[e] = s
+            self.expert_in[s] = e
         if preload:
             for s in range(S):
                 self.slot_of[s] = s
@@ -34,10 +39,11 @@ class MoveToFront:
         P = [int(e) for e in np.asarray(ids).reshape(-1)]
         M = np.asarray(ids).shape[0]
         U = list(dict.fromkeys(P))
-        if M > 16 or len(U) > self.S:
+        free = self.S - len(self.pinned)
+        if M > 16 or len([e for e in U if e not in self.pinned]) > free:
             return True, []
         hits = {e for e in U if e in self.slot_of}
-        victims = [s for s in range(self.S) if self.expert_in[s] < 0]
+        victims = [s for s in range(len(self.pinned), self.S) if self.expert_in[s] < 0]
         victims += [self.slot_of[e] for e in self.recency if e not in hits]
         events = []
         for i, e in enumerate([e for e in U if e not in hits]):
@@ -53,7 +59,7 @@ class MoveToFront:
         for e in U:
             if e in self.recency:
                 self.recency.remove(e)
-        self.recency += sorted(U, key=lambda e: last[e])
+        self.recency += sorted([e for e in U if e not in self.pinned], key=lambda e: last[e])
         return False, events
 
 
@@ -81,6 +87,62 @@ def test_matches_move_to_front(E, S, k, preload):
             for e in rec.uniques:
                 assert st.e2s[e] >= 0
     assert st.t == 2500
+
+
+@pytest.mark.parametrize("E,S,k,npin", [(6, 3, 1, 1), (8, 4, 2, 2), (9, 5, 2, 3), (8, 4, 3, 4), (10, 6, 2, 5)])
+def test_pinned_slots_match_move_to_front(E, S, k, npin):
+    """Hybrid policy: npin experts pinned in the first slots, LRU over the rest,
+    against the key-free recency list (bypass decisions and every event)."""
+    rng = np.random.default_rng(E * 31 + S * 7 + npin)
+    pins = [int(e) for e in rng.choice(E, size=npin, replace=False)]
+    st = SlotState(E, S, k)
+    st.pin(pins)
+    mtf = MoveToFront(E, S, pins=pins)
+    for t in range(2500):
+        M = int(rng.choice([1, 1, 1, 2, 3, 17]))
+        ids = _random_ids(rng, E, k, M)
+        rec = st.step(ids)
+        bypass, events = mtf.step(ids)
+        assert rec.bypass == bypass, t
+        assert rec.events == events, (t, ids)
+        st.check_invariants()
+        assert [st.s2e[s] for s in range(npin)] == pins      # pinned slots never change
+        if not rec.bypass:
+            for e in rec.uniques:
+                assert st.e2s[e] >= 0
+
+
+def test_all_slots_pinned_is_the_static_pin():
+    """P = S: a step is cached exactly when all its experts are pinned, nothing
+    is ever filled, and the resident fraction of all lookups (hits on cached
+    steps plus residents of bypass steps, whose host bytes exclude them) equals
+    the static-pin hit rate of the same pinned set."""
+    from oracle import static_pin, static_pin_hit_rate
+    rng = np.random.default_rng(21)
+    E, S, k, B = 12, 5, 2, 1000
+    trace = [_random_ids(rng, E, k, int(rng.choice([1, 1, 2, 3]))) for _ in range(1500)]
+    uniques = [list(dict.fromkeys(int(e) for e in ids.reshape(-1))) for ids in trace]
+    pin = static_pin(uniques, E, S)
+    st = SlotState(E, S, k, blob_bytes=B)
+    st.pin(pin)
+    for ids, u in zip(trace, uniques):
+        rec = st.step(ids)
+        assert rec.bypass == (not set(u) <= set(pin))
+        assert rec.events == []
+    c = st.counters
+    total = sum(len(u) for u in uniques)
+    resident = c.hits + sum(len(u) for u in uniques) - c.lookups - c.bypass_bytes // B
+    assert c.misses == 0 and c.bytes_filled == 0
+    assert resident / total == pytest.approx(static_pin_hit_rate(uniques, E, S), abs=0)
+
+
+def test_bypass_reads_only_non_resident_experts():
+    """A bypass step's host bytes count its non-resident unique experts only."""
+    st = SlotState(4, 2, 2, blob_bytes=10)
+    st.step(np.array([[0, 1]]))                 # fills slots with 0, 1
+    rec = st.step(np.array([[0, 2], [3, 1]]))   # U = 0,2,3,1 > S: bypass; 0 and 1 resident
+    assert rec.bypass
+    assert st.counters.bypass_bytes == 2 * 10
 
 
 def test_victim_has_the_minimum_key():
