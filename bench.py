@@ -387,6 +387,10 @@ def main():
                       "achieved_GBs": round(filled / (fill_time_miss * 1e-6) / 1e9, 2) if fill_time_miss > 0 else None,
                       "peak_GBs": PCIE_PEAK_GBS},
         "wall_s_timed_region": wall,
+        # the pages' decode token model ("GLM 5.3 Testing: HBM Expert Allocation", section "What the physics
+        # says to expect"): every token runs each of the 75 MoE layers once, plus ~3 ms of non-MoE work
+        "token_model": {"n_moe_layers": 75, "us_per_layer_step": round(graph_us, 3), "other_ms": 3.0,
+                        "tok_per_s": round(1000.0 / (75 * graph_us / 1000.0 + 3.0), 2)},
     }
     if not a.no_cpu_baseline:
         print("bench: timing the oracle on a bounded CPU sample", file=sys.stderr, flush=True)

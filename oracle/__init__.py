@@ -21,12 +21,14 @@ from .blob import part_layout, blob_size, dequant_expert
 from .routing import route
 from .lru import SlotState, StepRecord, Counters
 from .static_pin import static_pin, static_pin_hit_rate
+from .policy import lru_hit_curve, lru_hits_by_simulation, allocate_slots, hybrid_curve, token_rate
 from .expert import silu, expert_apply, layer_output
 from .layer import OracleLayer
 
 __all__ = [
     "E2M1_TABLE", "e2m1_value", "e4m3_value", "bf16_value", "decode_e2m1", "decode_e4m3",
     "decode_bf16", "part_layout", "blob_size", "dequant_expert", "route", "SlotState",
-    "StepRecord", "Counters", "static_pin", "static_pin_hit_rate", "silu", "expert_apply",
+    "StepRecord", "Counters", "static_pin", "static_pin_hit_rate", "lru_hit_curve", "lru_hits_by_simulation",
+    "allocate_slots", "hybrid_curve", "token_rate", "silu", "expert_apply",
     "layer_output", "OracleLayer",
 ]
