@@ -4,8 +4,8 @@
 // Method: the slot cache of page "GLM 5.3 Testing: HBM Expert Allocation"
 // (section "What the slot cache is": ids are mapped to slots on the device
 // before the expert launch, a miss takes the least-recently-used victim slot,
-// more than 16 rows bypass), replacing the "dozen tiny torch ops" of that
-// page's section "The build" with one kernel.  Occupancy is a live LRU clock
+// more than 16 rows bypass), doing in one kernel what that page's section "The
+// build" spread over a dozen small framework ops.  Occupancy follows an LRU clock
 // (page "GB300 GLM 5.3 Testing", section "Expert allocation vs a cache").
 // Router ties break by a stable expert order (page "TensorFold GLM-5.3
 // explained", exact-decoding rule).

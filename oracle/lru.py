@@ -4,7 +4,7 @@ Pages: each MoE layer owns S fixed HBM slots; router ids are mapped to slot ids
 on the device before the single expert launch; a missing expert is copied into
 the least-recently-used victim slot and the map is updated (page "GLM 5.3
 Testing: HBM Expert Allocation", sections "What the slot cache is" and the
-shelf analogy after it).  Occupancy follows a live LRU clock and the per-layer
+shelf analogy after it).  Occupancy follows a running LRU clock and the per-layer
 slot map only sets the capacity (page "GB300 GLM 5.3 Testing", section "Expert
 allocation vs a cache").  Batches of more than 16 rows bypass the cache and read
 experts directly (same section on the HBM allocation page).
@@ -18,8 +18,8 @@ bookkeeping is per step, not per pick):
     or when its unique experts do not fit: |U| > S.  A bypass step reads only
     its non-resident experts from the host store; resident ones are read from
     their slots (page "GB300 GLM 5.3 Testing", section on sizing the context
-    window: the bypass path reads non-resident experts per chunk), so its host
-    bytes are (non-resident unique experts) * B_e.
+    window: the bypass path fetches only experts that are not resident), so
+    its host bytes are (non-resident unique experts) * B_e.
   * Pinned slots (the hybrid policy; page "GB300 GLM 5.3 Testing", section
     "Expert allocation vs a cache", compares pins with LRU): the first P slots
     hold a fixed expert each and are never victims; LRU runs over the other

@@ -1,7 +1,7 @@
 """Slot-budget and placement policies over routing traces (test infrastructure).
 
 Page "GB300 GLM 5.3 Testing": a per-layer slot count is a capacity, occupancy
-is a live LRU clock, and a hindsight static pin is the comparator (section
+follows an LRU clock, and a hindsight static pin is the comparator (section
 "Expert allocation vs a cache"); the slot map should come from the routing
 traces by transfer bytes saved per HBM byte, with fewer slots for flat layers
 (page "GLM 5.3 Testing: HBM Expert Allocation", section "What's next, in
