@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--sweep-rows", default="",
                     help="comma-separated M values: all-hit GLM layer (every expert resident), drafted rows; "
                          "prints one JSON line per M instead of the headline line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="only time M=64 prefill chunks on the GLM layer (128 slots warmed by 64 one-row steps), "
+                         "staged 64 experts at a time and read in place; prints one JSON line")
     ap.add_argument("--dump-steps", default="",
                     help="write the timed steps' all-hit indices and gate/up event durations to this JSON file")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "STEPS_JSON"),
@@ -198,6 +201,52 @@ def trace_summary(trace_csv, steps_json):
                       "rocprof_avg_us_all_launches": round(float(np.mean(dur)), 3)}))
 
 
+def prefill(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace):
+    """M=64 prefill chunks on the GLM layer (128 slots warmed by 64 one-row steps): resident
+    experts come from their slots, the others are staged into HBM 64 at a time (the default)
+    or read in place from pinned host memory (prefill_stage=0).  One JSON line."""
+    cfg = CONFIGS["glm"]
+    dev = torch.device("cuda:0")
+    W, K, M = 64, min(a.steps, 20), 64
+    logits, _ = routing_trace(cfg, 0, steps=W + K * M)
+    d_l = torch.from_numpy(logits[:, :1].copy()).to(dev)          # [T, 1, E]
+    x1 = torch.from_numpy(np.stack([activations(cfg, 0, t, 1) for t in range(W)]).view(np.int16)).to(dev)
+    # a prefill chunk: the next 64 positions of the same routing stream, one row each
+    chunks = [torch.from_numpy(logits[W + i * M:W + (i + 1) * M, 0].copy()).to(dev) for i in range(K)]
+    xs = torch.from_numpy(activations(cfg, 0, 10_000, M).view(np.int16)).to(dev)
+    out = {"prefill": "GLM layer, 128 slots warmed by %d one-row steps, then %d chunks of M=%d rows" % (W, K, M),
+           "steps": K}
+    ys = {}
+    for G in (64, 0):
+        sc = SlotCache(1, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.slots, M, prefill_stage=G)
+        expert_blobs(cfg, 0, out=sc.backing(0))
+        sc.set_global_scales(0, global_scales(cfg, 0, "unit"))
+        y = torch.empty((M, cfg.hidden), dtype=torch.float32, device=dev)
+        for t in range(W):
+            sc.decode(0, d_l[t], x1[t], y[:1])
+        sc.decode(0, chunks[0], xs, y)      # untimed first chunk
+        torch.cuda.synchronize()
+        st0 = sc.stats(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(1, K):
+            sc.decode(0, chunks[i], xs, y)
+        e1.record()
+        torch.cuda.synchronize()
+        st1 = sc.stats(0)
+        ys[G] = y.clone()
+        us = e0.elapsed_time(e1) * 1e3 / (K - 1)
+        host = (st1["bypass_bytes"] - st0["bypass_bytes"]) / (K - 1)
+        out["staged_64" if G else "in_place"] = {
+            "us_per_step": round(us, 1), "host_experts_per_step": round(host / sc.blob_bytes, 2),
+            "host_GBs": round(host / (us * 1e-6) / 1e9, 2),
+            "tok_per_s_one_layer": round(M / (us * 1e-6), 1)}
+        sc.close()
+    out["speedup"] = round(out["in_place"]["us_per_step"] / out["staged_64"]["us_per_step"], 3)
+    out["bit_equal"] = bool(torch.equal(ys[64], ys[0]))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.trace_summary:
@@ -222,6 +271,9 @@ def main():
 
     if a.sweep_rows:
         sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace)
+        return
+    if a.prefill:
+        prefill(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace)
         return
     cfg = CONFIGS[a.config]
     if cfg.rows != 1 or cfg.n_layers != 1:

@@ -43,6 +43,7 @@ class sc_config(ctypes.Structure):
         ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("slots_per_layer", ctypes.POINTER(ctypes.c_int32)), ("max_rows", ctypes.c_int32),
         ("n_banks", ctypes.c_int32), ("event_capacity", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("prefill_stage", ctypes.c_int32),
     ]
 
 
@@ -111,11 +112,11 @@ def _check(st):
 
 
 def make_config(n_layers, hidden, inter, n_experts, top_k, slots_per_layer, max_rows,
-                n_banks=1, event_capacity=0, flags=0):
+                n_banks=1, event_capacity=0, flags=0, prefill_stage=0):
     arr = (ctypes.c_int32 * n_layers)(*[int(s) for s in slots_per_layer])
     cfg = sc_config(n_layers, hidden, inter, n_experts, top_k,
                     ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), max_rows, n_banks,
-                    event_capacity, flags)
+                    event_capacity, flags, prefill_stage)
     cfg._keep = arr
     return cfg
 

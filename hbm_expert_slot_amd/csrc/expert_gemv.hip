@@ -52,7 +52,26 @@ struct GemvArgs {
   int64_t code_off;      // offset of the code rows inside a blob
   int64_t scale_off;     // offset of the scale rows inside a blob
   uint64_t* span;        // execution stamps of a timed step, else null
+  const int32_t* order;  // staged prefill: unique experts in group order
+  int group;             // -1: every unique expert; g >= 0: group g of a staged step
+  int G;                 // experts per staged group
 };
+
+// The unique experts a launch computes: positions [lo, lo + n) of `order`, or
+// all U in their own order when the launch is not one group of a staged step.
+__device__ __forceinline__ void launch_uniques(const GemvArgs& a, int U, int& lo, int& n) {
+  if (a.group < 0) {
+    lo = 0;
+    n = U;
+  } else {
+    int hi;
+    group_range(a.hdr, a.group, a.G, lo, hi);
+    n = hi - lo;
+  }
+}
+__device__ __forceinline__ int unique_at(const GemvArgs& a, int lo, int j) {
+  return a.group < 0 ? j : a.order[lo + j];
+}
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
@@ -273,7 +292,9 @@ struct Gemv {
 
   __device__ static __forceinline__ void run(const GemvArgs& a) {
     static_assert(!SINGLE || MR == 1, "one-row steps have one pick per expert");
-    const int U = SINGLE ? a.k : a.hdr[H_UNIQUE];
+    int lo = 0, U = a.k;
+    if (!SINGLE) launch_uniques(a, a.hdr[H_UNIQUE], lo, U);
+    if (U <= 0) return;
     const int lane = threadIdx.x & 63;
     const int seg = lane % LPR, rsub = lane / LPR;
     const int nwaves = gridDim.x * (kGemvThreads / 64);
@@ -285,7 +306,8 @@ struct Gemv {
     const int per = (spu + wpu - 1) / wpu;
     const int ntask = U * wpu;
     for (int task = gw; task < ntask; task += nwaves) {
-      const int u = task / wpu, sub = task - (task / wpu) * wpu;
+      const int j = task / wpu, sub = task - (task / wpu) * wpu;
+      const int u = SINGLE ? j : unique_at(a, lo, j);
       // a task owns row steps base + i * stride, i < n
       int base, stride, n;
       if (STRIDED) {
@@ -394,7 +416,8 @@ struct GemvMfma {
   static constexpr int NM = GATEUP ? 2 : 1;
 
   __device__ static __forceinline__ void run(const GemvArgs& a) {
-    const int U = a.hdr[H_UNIQUE];
+    int lo, U;
+    launch_uniques(a, a.hdr[H_UNIQUE], lo, U);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, n = lane & 15;
     const int nwaves = gridDim.x * (kGemvThreads / 64);
@@ -403,7 +426,7 @@ struct GemvMfma {
     const int tpu = (ntiles + RT - 1) / RT;     // tasks per unique expert
     const int ntask = U * tpu;
     for (int task = gw; task < ntask; task += nwaves) {
-      const int u = task / tpu, tg = task - (task / tpu) * tpu;
+      const int u = unique_at(a, lo, task / tpu), tg = task - (task / tpu) * tpu;
       const uint8_t* blob = a.uniq_ptr[u];
       const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
       const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
@@ -494,15 +517,25 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvArgs a) {
   span_end(a.span);
 }
 
-// Copies the step's missed blobs (host-mapped pinned memory -> HBM slots).
-// The misses' 16-byte chunks form one index space so every thread keeps
-// four loads in flight across blob boundaries; with no misses it exits.
-// Entries whose destination is null (a miss the remap could not place) are
-// skipped.
+// Copies the step's missed blobs (host-mapped pinned memory -> HBM slots), or
+// one group of a staged prefill step's experts into the staging blobs (group
+// >= 0).  The copies' 16-byte chunks form one index space so every thread
+// keeps four loads in flight across blob boundaries; with nothing to copy it
+// exits.  Entries whose destination is null (a miss the remap could not
+// place) are skipped.
 __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t* const* src,
-                                               uint8_t* const* dst, long n16, uint64_t* span) {
+                                               uint8_t* const* dst, long n16, int group, int G, uint64_t* span) {
   span_start(span);
-  const long total = (long)hdr[H_MISS] * n16;
+  int first = 0, count = hdr[H_MISS];
+  if (group >= 0) {
+    const int ns = hdr[H_STAGED];
+    first = group * G;
+    count = ns < first + G ? ns - first : G;
+    if (count < 0) count = 0;
+  }
+  src += first;
+  dst += first;
+  const long total = (long)count * n16;
   const long stride = (long)gridDim.x * blockDim.x;
   long o = (long)blockIdx.x * blockDim.x + threadIdx.x;
   for (; o + 3 * stride < total; o += 4 * stride) {
@@ -643,13 +676,13 @@ bool gemv_supported(int K, bool gateup) {
   return gateup ? pick_gemv<true, 0>(K) != nullptr : pick_gemv<false, 0>(K) != nullptr;
 }
 
-hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev) {
+hipError_t launch_fill(const Shape& sh, const Workspace& W, int group, hipStream_t st, KEvents ev) {
   return sc_launch(k_fill, dim3(kFillBlocks), dim3(256), st, ev, (const int32_t*)W.hdr,
-                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16),
-                   ev.span_for(kFillBlocks));
+                   (const uint8_t* const*)W.miss_src, (uint8_t* const*)W.miss_dst, (long)(sh.blob / 16), group,
+                   (int)W.stage_n, ev.span_for(kFillBlocks));
 }
 
-static GemvArgs base_args(const Workspace& W, const float* gs) {
+static GemvArgs base_args(const Workspace& W, const float* gs, int group) {
   GemvArgs a;
   a.hdr = W.hdr;
   a.uniq_ptr = W.uniq_ptr;
@@ -658,12 +691,15 @@ static GemvArgs base_args(const Workspace& W, const float* gs) {
   a.uniq_off = W.uniq_off;
   a.uniq_picks = W.uniq_picks;
   a.span = nullptr;
+  a.order = W.uniq_order;
+  a.group = group;
+  a.G = W.stage_n;
   return a;
 }
 
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
-                         bool mfma, hipStream_t st, KEvents ev) {
-  GemvArgs a = base_args(W, gs);
+                         bool mfma, int group, hipStream_t st, KEvents ev) {
+  GemvArgs a = base_args(W, gs, group);
   a.operand = x;
   a.out = W.h;
   a.rows = sh.I;
@@ -688,9 +724,9 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
 }
 
-hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, hipStream_t st,
-                       KEvents ev) {
-  GemvArgs a = base_args(W, gs);
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, int group,
+                       hipStream_t st, KEvents ev) {
+  GemvArgs a = base_args(W, gs, group);
   a.operand = W.h;
   a.out = W.part;
   a.rows = sh.H;

@@ -25,7 +25,8 @@ enum Counter {
 };
 
 // Workspace header words.
-enum Hdr { H_UNIQUE = 0, H_MISS = 1, H_BYPASS = 2, H_ROWS = 3, H_WORDS = 64 };
+// H_RESIDENT / H_STAGED: a staged prefill step's resident and staged unique experts.
+enum Hdr { H_UNIQUE = 0, H_MISS = 1, H_BYPASS = 2, H_ROWS = 3, H_RESIDENT = 4, H_STAGED = 5, H_WORDS = 64 };
 
 // Device view of one layer: its maps, clock, counters, event ring, slots,
 // the backing bank it reads and that bank's global-scale table.
@@ -60,7 +61,29 @@ struct Workspace {
   uint8_t** miss_dst;           // [Pmax]
   float* h;                     // [Pmax][I]  SiLU(gate) * up, per pick
   float* part;                  // [Pmax][H]  down projection, per pick
+  int32_t* uniq_order;          // [Pmax]  staged prefill: resident uniques, then staged ones in staging order
+  uint8_t* stage;               // [stage_n] blobs: prefill staging area (null when stage_n == 0)
+  int32_t stage_n;              // G, experts per prefill group (0: no staging)
 };
+
+// A step of M rows is staged when it is a prefill chunk and the workspace has
+// a staging area.
+__host__ __device__ inline bool staged_step(const Workspace& W, int M) { return M > kCachedRows && W.stage_n > 0; }
+// Groups enqueued for a staged step: enough for min(M*k, E) staged experts.
+inline int stage_groups(const Workspace& W, int M, int k, int E) {
+  const int maxu = M * k < E ? M * k : E;
+  return (maxu + W.stage_n - 1) / W.stage_n;
+}
+
+// Positions [lo, hi) of group `g` in uniq_order: the resident experts and the
+// first G staged ones form group 0, staged ones g*G .. g*G+G-1 group g.
+__device__ __forceinline__ void group_range(const int32_t* hdr, int g, int G, int& lo, int& hi) {
+  const int nres = hdr[H_RESIDENT], ns = hdr[H_STAGED];
+  const int end = ns < (g + 1) * G ? ns : (g + 1) * G;
+  lo = g == 0 ? 0 : nres + g * G;
+  hi = nres + end;
+  if (hi < lo) hi = lo;
+}
 
 struct Shape {
   int32_t H, I, E, k;
@@ -126,12 +149,14 @@ bool gemv_supported(int K, bool gateup);
 // Enqueue the phases of one step.  Each returns hipSuccess or the launch error.
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
                         const float* logits, int M, hipStream_t st, KEvents ev);
-hipError_t launch_fill(const Shape& sh, const Workspace& W, hipStream_t st, KEvents ev);
+// group: -1 for a whole step (the step's misses / all its unique experts),
+// g >= 0 for group g of a staged prefill step.
+hipError_t launch_fill(const Shape& sh, const Workspace& W, int group, hipStream_t st, KEvents ev);
 // mfma: the matrix-core kernels may serve M >= 12 (off: the streaming kernels for every M).
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
-                         bool mfma, hipStream_t st, KEvents ev);
-hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, hipStream_t st,
-                       KEvents ev);
+                         bool mfma, int group, hipStream_t st, KEvents ev);
+hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, int group,
+                       hipStream_t st, KEvents ev);
 hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,
                           KEvents ev);
 

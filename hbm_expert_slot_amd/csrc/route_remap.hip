@@ -19,7 +19,8 @@
 //          advances, resident experts are read from their slots and the
 //          others from the backing store (the pages' bypass reads
 //          non-resident experts: page "GB300 GLM 5.3 Testing", section on
-//          sizing the context window)
+//          sizing the context window); a prefill step with a staging area
+//          copies those into HBM staging blobs first, G per group
 //   pinned slots [0, P) hold fixed experts and are never victims
 //   candidates = slots not holding a hit, ascending (key, slot); empty slots
 //          have key -1; the i-th miss (first-occurrence order) takes the i-th
@@ -344,7 +345,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     int tot, tot_pin;
     const int r = block_rank(ms, s_wc, &tot);
     (void)block_rank(pn, s_wc, &tot_pin);
-    if (u < U) s_umiss[u] = ms ? nmiss + r : -1;
+    // a miss stores its rank among misses; a resident expert -1 - its rank
+    // among resident ones (r counts the misses before u in either case)
+    if (u < U) s_umiss[u] = ms ? nmiss + r : -1 - (u - (nmiss + r));
     nmiss += tot;
     npin += tot_pin;
   }
@@ -451,8 +454,26 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       a.L.key[sl] = t * (int64_t)(kCachedRows * k) + (int64_t)s_last[s_uexp[u]];
       a.W.uniq_ptr[u] = a.L.slots + (size_t)sl * B;
     }
+  } else if (staged_step(a.W, M)) {
+    // staged prefill: resident experts from their slots; the i-th non-resident
+    // one is copied into staging blob i % G by group i / G.  uniq_order lists
+    // the resident experts, then the staged ones in staging order.
+    const int G = a.W.stage_n, nres = U - nmiss;
+    for (int u = tid; u < U; u += kRouteThreads) {
+      const int sl = s_uslot[u], i = s_umiss[u];
+      if (sl >= 0) {
+        a.W.uniq_ptr[u] = a.L.slots + (size_t)sl * B;
+        a.W.uniq_order[-1 - i] = u;
+      } else {
+        uint8_t* dst = a.W.stage + (size_t)(i % G) * B;
+        a.W.uniq_ptr[u] = dst;
+        a.W.miss_src[i] = a.L.backing + (size_t)s_uexp[u] * B;
+        a.W.miss_dst[i] = dst;
+        a.W.uniq_order[nres + i] = u;
+      }
+    }
   } else {
-    // bypass: resident experts from their slots, the others from the backing store
+    // bypass: resident experts from their slots, the others read in place from the backing store
     for (int u = tid; u < U; u += kRouteThreads) {
       const int sl = s_uslot[u];
       a.W.uniq_ptr[u] = sl >= 0 ? a.L.slots + (size_t)sl * B : a.L.backing + (size_t)s_uexp[u] * B;
@@ -496,6 +517,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     a.W.hdr[H_MISS] = bypass ? 0 : nmiss;     // a bypass step fills nothing
     a.W.hdr[H_BYPASS] = bypass ? 1 : 0;
     a.W.hdr[H_ROWS] = M;
+    a.W.hdr[H_RESIDENT] = U - nmiss;
+    a.W.hdr[H_STAGED] = bypass && staged_step(a.W, M) ? nmiss : 0;
     cnt[C_STEPS] += 1;
     if (bypass) {
       cnt[C_BYPASS] += 1;

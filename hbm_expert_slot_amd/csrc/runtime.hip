@@ -62,7 +62,7 @@ LayerOffsets layer_offsets(int E, int S, int cap) {
 
 struct WsOffsets {
   size_t hdr, pick_expert, pick_w, pick_u, uniq_expert, uniq_ptr, uniq_off, uniq_picks,
-      miss_src, miss_dst, h, part, span, end;
+      miss_src, miss_dst, h, part, span, uniq_order, stage, end;
 };
 
 // Blocks of a launch whose execution stamps are kept: the GEMV grids are
@@ -73,7 +73,10 @@ int span_blocks(int Pmax_rows, int H) {
   return (int)(comb > 2048 ? comb : 2048);
 }
 
-WsOffsets ws_offsets(int Pmax, int H, int I, int max_rows) {
+// Experts the prefill staging area holds (none when no step can be a prefill chunk).
+int stage_experts(const sc_config* c) { return c->max_rows > kCachedRows ? c->prefill_stage : 0; }
+
+WsOffsets ws_offsets(int Pmax, int H, int I, int max_rows, int stage_n, int64_t blob) {
   WsOffsets o;
   size_t p = 0;
   o.hdr = p; p = align_up(p + H_WORDS * 4);
@@ -89,6 +92,8 @@ WsOffsets ws_offsets(int Pmax, int H, int I, int max_rows) {
   o.h = p; p = align_up(p + (size_t)Pmax * I * 4);
   o.part = p; p = align_up(p + (size_t)Pmax * H * 4);
   o.span = p; p = align_up(p + (size_t)SC_N_KERNELS * span_blocks(max_rows, H) * kSpanSlots * 8);
+  o.uniq_order = p; p = align_up(p + (size_t)Pmax * 4);
+  o.stage = p; p = align_up(p + (size_t)stage_n * (size_t)blob);
   o.end = p;
   return o;
 }
@@ -114,6 +119,8 @@ sc_status check_config(const sc_config* c) {
   if (c->n_banks < 1 || c->n_banks > c->n_layers) return fail(SC_E_ARG, "n_banks must be in [1, n_layers]");
   if (c->event_capacity < 0) return fail(SC_E_ARG, "event_capacity must be >= 0");
   if (c->flags & ~(uint32_t)SC_FLAG_BATCH_INVARIANT) return fail(SC_E_ARG, "unknown flags 0x%x", c->flags);
+  if (c->prefill_stage < 0 || c->prefill_stage > kMaxExperts)
+    return fail(SC_E_ARG, "prefill_stage must be in [0, %d]", kMaxExperts);
   if (!c->slots_per_layer) return fail(SC_E_ARG, "slots_per_layer is NULL");
   for (int l = 0; l < c->n_layers; ++l) {
     int S = c->slots_per_layer[l];
@@ -180,7 +187,7 @@ Sizes compute_sizes(const sc_config* c) {
   state += align_up((size_t)c->n_banks * c->n_experts * 2 * sizeof(float));
   z.pool = pool;
   z.state = state;
-  z.wo = ws_offsets(c->max_rows * c->top_k, c->hidden, c->inter, c->max_rows);
+  z.wo = ws_offsets(c->max_rows * c->top_k, c->hidden, c->inter, c->max_rows, stage_experts(c), sh.blob);
   z.ws = z.wo.end;
   z.bank = (size_t)c->n_experts * (size_t)sh.blob;
   return z;
@@ -309,6 +316,9 @@ sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
   h->W.miss_dst = reinterpret_cast<uint8_t**>(ws + o.miss_dst);
   h->W.h = reinterpret_cast<float*>(ws + o.h);
   h->W.part = reinterpret_cast<float*>(ws + o.part);
+  h->W.uniq_order = reinterpret_cast<int32_t*>(ws + o.uniq_order);
+  h->W.stage_n = stage_experts(cfg);
+  h->W.stage = h->W.stage_n > 0 ? ws + o.stage : nullptr;
   h->d_span = reinterpret_cast<uint64_t*>(ws + o.span);
   h->span_cap = span_blocks(cfg->max_rows, cfg->hidden);
   h->timed = false;
@@ -441,11 +451,22 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
     }
     return k;
   };
-  e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
-  if (e == hipSuccess) e = launch_fill(h->sh, h->W, s, kev(1));
   const bool mfma = !(h->cfg.flags & SC_FLAG_BATCH_INVARIANT);
-  if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, s, kev(2));
-  if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, s, kev(3));
+  e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
+  if (!staged_step(h->W, M)) {
+    if (e == hipSuccess) e = launch_fill(h->sh, h->W, -1, s, kev(1));
+    if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, -1, s, kev(2));
+    if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, -1, s, kev(3));
+  } else {
+    // prefill groups: copy G experts into staging, compute them, next group
+    const int ng = stage_groups(h->W, M, h->sh.k, h->sh.E);
+    for (int g = 0; g < ng && e == hipSuccess; ++g) {
+      auto gev = [&](int i) { return g == 0 ? kev(i) : KEvents(); };
+      e = launch_fill(h->sh, h->W, g, s, gev(1));
+      if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, g, s, gev(2));
+      if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, g, s, gev(3));
+    }
+  }
   if (e == hipSuccess) e = launch_combine(h->sh, h->W, d_y, M, s, kev(4));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   h->last_stream = s;

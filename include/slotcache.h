@@ -84,7 +84,22 @@ typedef struct {
   int32_t n_banks;                /* host backing banks, 1..n_layers; layer l reads bank l % n_banks */
   int32_t event_capacity;         /* per-layer miss-event ring, records (0 = 4096) */
   uint32_t flags;                 /* 0 or SC_FLAG_BATCH_INVARIANT */
+  int32_t prefill_stage;          /* G, experts staged per prefill group, 0..1024 (see below) */
 } sc_config;
+
+/* Prefill groups.  A step of more than SC_BYPASS_ROWS rows (a prefill chunk)
+ * always bypasses the cache.  With prefill_stage = 0 its non-resident experts
+ * are read in place from the host-mapped backing store by the expert kernels.
+ * With G = prefill_stage > 0 the workspace holds a G-blob staging area in HBM:
+ * the step's non-resident experts, in first-occurrence order, are copied into
+ * it G at a time by the fill kernel, and each group's expert products (the
+ * resident experts go with the first group) run from HBM before the next
+ * group is copied; the weighted combine runs once, after the last group, so
+ * the output is the same bits as without staging.  The pages' prefill-groups
+ * knob stages 64 experts at a time and reduces once (page "glm53 -
+ * GLM-5.3-Flash (NVFP4)").  A step of M rows enqueues ceil(min(M*k, E) / G)
+ * groups; groups left empty exit at once.  Ignored (no staging area) when
+ * max_rows <= SC_BYPASS_ROWS. */
 
 /* Every row of a step computes the bits it would compute alone, as a one-row
  * step: the streaming FP4 kernels run for every M (their per-row reduction
@@ -98,7 +113,8 @@ typedef struct {
   size_t blob_bytes;              /* B_e */
   size_t slot_pool_bytes;         /* device: sum over layers of S_l * B_e; 256-B aligned base */
   size_t state_bytes;             /* device: maps, LRU keys, counters, event rings, global scales */
-  size_t workspace_bytes;         /* device: per-call scratch shared by all layers */
+  size_t workspace_bytes;         /* device: per-call scratch shared by all layers, with the
+                                     prefill staging area (G * B_e) when there is one */
   size_t backing_bytes_per_bank;  /* host, allocated by the library: E * B_e */
 } sc_sizes;
 
@@ -169,8 +185,9 @@ SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_lo
 #define SC_N_EVENTS (2 * SC_N_KERNELS)
 /* moe_layer_decode with per-kernel timing: events[2i] and events[2i+1]
  * (hipEvent_t passed as void*, created by the caller) are stamped at the start
- * and the end of kernel i's execution (hipExtLaunchKernelGGL).  events == NULL
- * is moe_layer_decode. */
+ * and the end of kernel i's execution (hipExtLaunchKernelGGL).  On a staged
+ * prefill step the fill, gate/up and down events and spans are those of the
+ * first group's launches.  events == NULL is moe_layer_decode. */
 SC_API sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits,
                               const uint16_t* d_x, int32_t M, float* d_y, void* stream,
                               void* const* events);

@@ -481,3 +481,67 @@ def test_pinned_slots_against_the_oracle(shape):
     with pytest.raises(B.SlotCacheError):
         sc.write_state(0, bad_e2s, bad_s2e, key, step)      # pinned slots must keep their experts
     sc.close()
+
+
+@pytest.mark.parametrize("shape", ["tiny", "glm32"])
+def test_prefill_groups_match_in_place_reads(shape):
+    """Prefill chunks (M > 16) with their non-resident experts staged into HBM G
+    at a time (G = 1, a ragged G and 64) produce the same bits as the in-place
+    host reads (G = 0), with the same bookkeeping; the staged run also matches
+    the oracle.  Cached steps in between keep some experts resident, so the
+    first group mixes slot-resident and staged experts.  A timed staged step
+    computes the same bits as well."""
+    torch = torch_cuda()
+    from hbm_expert_slot_amd import binding as B
+    cfg = CONFIGS["tiny"]
+    Ms, Gs, steps = [1, 2, 17, 4, 32, 1, 24, 3, 32, 1], [0, 1, 3, 64], 30
+    if shape == "glm32":
+        g = CONFIGS["glm"]
+        cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 12, rows=24, steps=12, seed=g.seed)
+        Ms, Gs, steps = [1, 2, 24, 1, 17, 4, 24, 1, 20, 1, 24, 2], [0, 5, 64], 12
+    maxM = max(Ms)
+    log("prefill groups vs in-place reads: %s, G in %s, %d steps" % (shape, Gs, steps))
+    E = cfg.n_experts
+    caches = {G: make_cache(cfg, max_rows=maxM, prefill_stage=G) for G in Gs}
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(29)
+    sample = None if shape == "tiny" else {2, 4, 6}
+    worst = 0.0
+    for t in range(steps):
+        M = Ms[t % len(Ms)]
+        z = rng.standard_normal((M, E)).astype(np.float32)
+        z[:, : cfg.top_k] += 0.8
+        x = activations(cfg, 0, 500 + t, M)
+        zd = torch.from_numpy(z).cuda()
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        ys = {}
+        for G, sc in caches.items():
+            y = torch.empty((M, cfg.hidden), dtype=torch.float32, device="cuda")
+            if G == Gs[-1] and M > 16:
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(B.SC_N_EVENTS)]
+                for ev in evs:
+                    ev.record()
+                sc.decode(0, zd, xd, y, events=evs)
+                torch.cuda.synchronize()
+                assert all(v > 0 for v in sc.kernel_spans())
+            else:
+                sc.decode(0, zd, xd, y)
+            ys[G] = y.cpu().numpy()
+        for G in Gs[1:]:
+            assert np.array_equal(ys[G], ys[0]), (t, M, G)
+        want_y = sample is None or t in sample
+        y_o, rec, ids_o, w_o = orc.decode(z, x, with_output=want_y)
+        if M > 16:
+            assert rec.bypass
+        if want_y:
+            r = rel_l2(ys[Gs[-1]], y_o)
+            assert r <= Y_TOL, (t, M, r)
+            worst = max(worst, r)
+    for G, sc in caches.items():
+        _check_state(sc, 0, orc.state)
+        _check_counters(sc, 0, orc.state)
+    st = caches[0].stats(0)
+    log("prefill groups %s: worst rel L2 %.3g, stats %s" % (shape, worst, st))
+    assert st["bypass_steps"] > 0 and st["bypass_bytes"] > 0 and st["hits"] > 0
+    for sc in caches.values():
+        sc.close()
