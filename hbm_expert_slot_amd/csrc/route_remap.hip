@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   __shared__ int s_uidx[kMaxExperts];
   __shared__ int s_uexp[kMaxExperts];
   __shared__ int s_uslot[kMaxExperts];
-  __shared__ int s_umiss[kMaxExperts];   // miss rank per unique; later CSR offsets
+  __shared__ int s_umiss[kMaxExperts];   // miss rank per unique (-1 - rank among resident ones); later CSR offsets
   __shared__ int s_victim[kMaxSlots];
   __shared__ int s_e2s[kMaxExperts];     // snapshot of the slot map
   __shared__ int s_s2e[kMaxSlots];

@@ -47,6 +47,17 @@ def test_sizes_for_the_glm_layer():
     assert s2.slot_pool_bytes == (8 + 16 + 256) * 21_233_664
 
 
+def test_prefill_staging_area_is_part_of_the_workspace():
+    """G staged blobs are added to the workspace when prefill chunks (more than 16 rows) can occur."""
+    base = B.slotcache_query_sizes(_cfg(prefill_stage=0)).workspace_bytes
+    for G in (1, 64, 1024):
+        ws = B.slotcache_query_sizes(_cfg(prefill_stage=G)).workspace_bytes
+        assert G * 21_233_664 <= ws - base < G * 21_233_664 + 256
+    # no prefill chunk can occur at max_rows <= 16: no staging area
+    assert (B.slotcache_query_sizes(_cfg(max_rows=16, prefill_stage=64)).workspace_bytes
+            == B.slotcache_query_sizes(_cfg(max_rows=16, prefill_stage=0)).workspace_bytes)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(top_k=0), B.SC_E_ARG),
     (dict(top_k=33), B.SC_E_ARG),
@@ -61,6 +72,8 @@ def test_sizes_for_the_glm_layer():
     (dict(hidden=3072), B.SC_E_UNSUPPORTED),
     (dict(inter=64), B.SC_E_UNSUPPORTED),
     (dict(flags=2), B.SC_E_ARG),
+    (dict(prefill_stage=-1), B.SC_E_ARG),
+    (dict(prefill_stage=1025), B.SC_E_ARG),
 ])
 def test_invalid_configs_are_rejected(kw, code):
     with pytest.raises(B.SlotCacheError) as ei:

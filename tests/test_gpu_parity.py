@@ -545,3 +545,44 @@ def test_prefill_groups_match_in_place_reads(shape):
     assert st["bypass_steps"] > 0 and st["bypass_bytes"] > 0 and st["hits"] > 0
     for sc in caches.values():
         sc.close()
+
+
+LIMIT_SHAPES = {
+    # the library's largest top-k, expert count, slot count and picks per step (max_rows * k = 2048)
+    "max": dict(E=1024, k=32, S=1024, Ms=[1, 2, 16, 1, 64, 16, 3, 64, 1], max_rows=64),
+    # one expert, one slot, top-1: every step after the first is a hit
+    "one_expert": dict(E=1, k=1, S=1, Ms=[1, 1, 4, 17, 1, 2], max_rows=17),
+    # every expert picked every step (k = E)
+    "k_eq_E": dict(E=8, k=8, S=8, Ms=[1, 2, 1, 17, 1], max_rows=17),
+    # one slot for two picks per row: every step bypasses
+    "one_slot": dict(E=16, k=2, S=1, Ms=[1, 1, 3, 1, 17], max_rows=17),
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape", list(LIMIT_SHAPES))
+def test_limit_shapes_against_the_oracle(shape):
+    """The compiled limits (E = 1024, k = 32, S = 1024, 2048 picks per step,
+    a 64-row step staged in 16 groups) and degenerate layers (one expert;
+    k = E; one slot for two picks) match the oracle's bookkeeping bit for bit
+    and its outputs to the tolerance."""
+    p = LIMIT_SHAPES[shape]
+    E, k, S, Ms = p["E"], p["k"], p["S"], p["Ms"]
+    cfg = WorkloadConfig("limit_" + shape, 256, 128, E, k, S, rows=p["max_rows"], steps=len(Ms), seed=41)
+    log("limit shapes: %s (E=%d k=%d S=%d, M in %s)" % (shape, E, k, S, Ms))
+    sc = make_cache(cfg, max_rows=p["max_rows"], gs_mode="uniform")
+    orc = _oracle_layer(cfg, S, "uniform")
+    rng = np.random.default_rng(43)
+    zs = [rng.standard_normal((max(Ms), E)).astype(np.float32) for _ in Ms]
+    for z in zs:
+        z[:, : max(1, E // 8)] += 1.0      # favourites, so that later steps hit
+    worst = _run_trace(cfg, sc, orc, len(Ms), lambda t: Ms[t], lambda t: zs[t])
+    st = sc.stats(0)
+    log("limit %s: worst rel L2 %.3g, stats %s" % (shape, worst, st))
+    if shape == "max":
+        assert st["misses"] > 512 and st["bypass_steps"] == 2
+    if shape == "one_slot":
+        assert st["bypass_steps"] == len(Ms)
+    if shape == "one_expert":
+        assert st["misses"] == 1 and st["hits"] == sum(1 for M in Ms if M <= 16) - 1
+    sc.close()
