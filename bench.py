@@ -172,8 +172,19 @@ def sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_s
         us = (times[0] - times[1]) * 1e3 / K
         uniq = (st1["lookups"] - st0["lookups"]) / max(1, st1["steps"] - st0["steps"])
         byts = uniq * sc.blob_bytes
+        # eager pass over the same steps: each kernel's execution span
+        spans = []
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(PHASES))]
+        for ev in evs:           # torch creates the HIP event on first record
+            ev.record(stream)
+        for t in range(K):
+            sink.copy_(flush.amax())
+            sc.decode(0, d_l[t], d_x[t], d_y[t], stream=stream, events=evs)
+            spans.append(sc.kernel_spans())
+        kus = np.mean(np.array(spans), axis=0)
         print(json.dumps({"sweep": "all-hit GLM layer, drafted rows", "M": M, "us_per_step": round(us, 2),
-                          "unique_experts_per_step": round(uniq, 2), "weight_GBs": round(byts / (us * 1e-6) / 1e9, 1)}), flush=True)
+                          "unique_experts_per_step": round(uniq, 2), "weight_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                          "kernels_us": {n: round(float(v), 2) for n, v in zip(PHASES, kus)}}), flush=True)
     sc.close()
 
 

@@ -415,6 +415,77 @@ struct GemvMfma {
   static_assert(K % 128 == 0, "K must be a multiple of 128");
   static constexpr int NKT = K / 128;
   static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int NX = GATEUP ? 4 : 8;     // 16-byte operand loads per lane and K tile
+
+  // One K tile of a task: the codes and block scales of its RT row tiles (gate
+  // and up for gate/up) and the lane's pick-column operand slice.
+  struct Stage {
+    uint4 q[RT][NM];
+    uint32_t sc[RT][NM];
+    uint4 x[NX];
+  };
+
+  // Every load is unconditional (no branches between the loads and their use,
+  // so the wait before a K tile's products covers that tile only): a ragged
+  // last task re-reads its last row tile for the tiles it does not have, and
+  // an idle pick column reads pick 0's operand row and zeroes it.
+  __device__ static __forceinline__ void load(Stage& st, const GemvArgs& a, const uint8_t* blob, int tile0, int nt,
+                                              const uint8_t* xsrc, bool live, int kt, int g, int n) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int tile = tile0 + (rt < nt ? rt : nt - 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const size_t row = (size_t)(tile * 16 + n + m * a.up_row0);
+        st.q[rt][m] = ld16_stream(blob + a.code_off + row * (K / 2) + 64 * kt + 16 * g);
+        st.sc[rt][m] = ld2(blob + a.scale_off + row * (K / 16) + 8 * kt + 2 * g);
+      }
+    }
+    // elements [128 kt + 32 g, +32) of the pick's operand row (bf16 x or fp32 h)
+    const uint8_t* src = xsrc + (size_t)(128 * kt + 32 * g) * (GATEUP ? 2 : 4);
+#pragma unroll
+    for (int v = 0; v < NX; ++v) {
+      const uint4 t = ld16(src + 16 * v);
+      st.x[v] = make_uint4(live ? t.x : 0u, live ? t.y : 0u, live ? t.z : 0u, live ? t.w : 0u);
+    }
+  }
+
+  __device__ static __forceinline__ void compute(const Stage& st, f32x4 (&acc)[RT][NM]) {
+    // B operand: elements [128 kt + 32 g + 8 q, +8) of pick column n for MFMA q
+    bf16x8 bh[4], bl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (GATEUP) {
+        bh[q] = bf16x8_from_words(st.x[q]);
+      } else {
+        const uint4 w0 = st.x[2 * q], w1 = st.x[2 * q + 1];
+        const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float hv = __uint_as_float(wv[j]);
+          const __bf16 hi = (__bf16)hv;
+          bh[q][j] = hi;
+          bl[q][j] = (__bf16)(hv - (float)hi);
+        }
+      }
+    }
+    // all RT tiles (a ragged task's extra tiles are computed and not stored)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const float s0 = __builtin_amdgcn_cvt_f32_fp8(st.sc[rt][m], 0);
+        const float s1 = __builtin_amdgcn_cvt_f32_fp8(st.sc[rt][m], 1);
+        const uint32_t d[4] = {st.q[rt][m].x, st.q[rt][m].y, st.q[rt][m].z, st.q[rt][m].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 av = fp4x8_scaled_bf16(d[q], q < 2 ? s0 : s1);
+          acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[q], acc[rt][m], 0, 0, 0);
+          if (!GATEUP) acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[q], acc[rt][m], 0, 0, 0);
+        }
+      }
+    }
+  }
 
   __device__ static __forceinline__ void run(const GemvArgs& a) {
     int lo, U;
@@ -428,6 +499,8 @@ struct GemvMfma {
     const int ntask = U * tpu;
     for (int task = gw; task < ntask; task += nwaves) {
       const int u = unique_at(a, lo, task / tpu), tg = task - (task / tpu) * tpu;
+      const int tile0 = tg * RT;
+      const int nt = ntiles - tile0 < RT ? ntiles - tile0 : RT;
       const uint8_t* blob = a.uniq_ptr[u];
       const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
       const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
@@ -435,75 +508,36 @@ struct GemvMfma {
         const int nc = off1 - c0 < 16 ? off1 - c0 : 16;
         const bool live = n < nc;
         const int p = live ? a.uniq_picks[c0 + n] : 0;
+        const uint8_t* xsrc = static_cast<const uint8_t*>(a.operand) +
+                              (GATEUP ? (size_t)(p / a.k) * K * 2 : (size_t)p * K * 4);
         f32x4 acc[RT][NM];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kt = 0; kt < NKT; ++kt) {
-          // B operand: elements [128kt + 32g, +32) of pick column n
-          bf16x8 bh[4], bl[4];
-          if (GATEUP) {
-            const uint16_t* src = static_cast<const uint16_t*>(a.operand) + (size_t)(p / a.k) * K + 128 * kt + 32 * g;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint4 v = live ? *reinterpret_cast<const uint4*>(src + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
-              bh[q] = bf16x8_from_words(v);
-            }
-          } else {
-            const float* src = static_cast<const float*>(a.operand) + (size_t)p * K + 128 * kt + 32 * g;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float hv[8];
-#pragma unroll
-              for (int h2 = 0; h2 < 2; ++h2) {
-                const float4 f = live ? *reinterpret_cast<const float4*>(src + 8 * q + 4 * h2)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-                hv[4 * h2 + 0] = f.x;
-                hv[4 * h2 + 1] = f.y;
-                hv[4 * h2 + 2] = f.z;
-                hv[4 * h2 + 3] = f.w;
-              }
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                const __bf16 hi = (__bf16)hv[j];
-                bh[q][j] = hi;
-                bl[q][j] = (__bf16)(hv[j] - (float)hi);
-              }
-            }
-          }
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const int tile = tg * RT + rt;
-            if (tile >= ntiles) break;
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const size_t row = (size_t)(tile * 16 + n + m * a.up_row0);
-              const uint4 q4 = ld16_stream(blob + a.code_off + row * (K / 2) + 64 * kt + 16 * g);
-              const uint32_t sc = ld2(blob + a.scale_off + row * (K / 16) + 8 * kt + 2 * g);
-              const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
-              const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
-              const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const bf16x8 av = fp4x8_scaled_bf16(d[q], q < 2 ? s0 : s1);
-                acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[q], acc[rt][m], 0, 0, 0);
-                if (!GATEUP) acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[q], acc[rt][m], 0, 0, 0);
-              }
-            }
-          }
+        // K tiles with the next tile's loads in flight while the current one is multiplied
+        Stage A, B;
+        load(A, a, blob, tile0, nt, xsrc, live, 0, g, n);
+        int kt = 0;
+        while (true) {
+          if (kt + 1 < NKT) load(B, a, blob, tile0, nt, xsrc, live, kt + 1, g, n);
+          compute(A, acc);
+          if (++kt >= NKT) break;
+          if (kt + 1 < NKT) load(A, a, blob, tile0, nt, xsrc, live, kt + 1, g, n);
+          compute(B, acc);
+          if (++kt >= NKT) break;
         }
         if (live) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const int tile = tg * RT + rt;
-            if (tile >= ntiles) break;
+            if (rt >= nt) break;
+            float v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int r = tile * 16 + 4 * g + j;
-              a.out[(size_t)p * a.rows + r] =
-                  GATEUP ? silu_f32(acc[rt][0][j] * gs) * (acc[rt][NM - 1][j] * gs) : acc[rt][0][j] * gs;
-            }
+            for (int j = 0; j < 4; ++j)
+              v[j] = GATEUP ? silu_f32(acc[rt][0][j] * gs) * (acc[rt][NM - 1][j] * gs) : acc[rt][0][j] * gs;
+            // rows 16 tile + 4 g .. + 3 of pick p: one 16-byte store
+            *reinterpret_cast<float4*>(a.out + (size_t)p * a.rows + (tile0 + rt) * 16 + 4 * g) =
+                make_float4(v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -644,12 +678,14 @@ constexpr int kDownBlocks = 512;
 
 int mr_for(int M) { return M == 1 ? 1 : 2; }
 
-// Rows per step from which the matrix-core path is used.  Measured on the
-// all-hit GLM layer with drafted rows: at M = 8 (about 27 unique experts, 2.4
-// picks each) the streaming path is faster (292 us against 358 us per step);
-// at M = 16 (about 46 unique experts) the matrix-core path is (511 against 643).
-constexpr int kMfmaMinRows = 12;
-constexpr int kMfmaTiles = 4;     // 16-row tiles per wavefront task
+// Rows per step from which each product runs on the matrix cores (all-hit GLM
+// layer, drafted rows, µs per kernel, streaming against matrix cores): gate/up
+// 141 / 160 at M = 8, 212 / 219 at 12, 268 / 232 at 14; down 39 / 46 at M = 2,
+// 62 / 50 at 3.  The two-pick streaming down kernel holds about 480 VGPRs (one
+// wavefront per SIMD), the matrix-core one about 180.
+constexpr int kMfmaMinRowsGateup = SC_MFMA_MIN_ROWS_GATEUP;
+constexpr int kMfmaMinRowsDown = SC_MFMA_MIN_ROWS_DOWN;
+constexpr int kMfmaTiles = 2;     // 16-row tiles per wavefront task (measured against 1 and 4)
 
 template <bool GATEUP>
 GemvFn pick_mfma(int K) {
@@ -713,7 +749,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.code_off = 0;
   a.scale_off = sh.off_w13s;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  if (mfma && M >= kMfmaMinRows) {
+  if (mfma && M >= kMfmaMinRowsGateup) {
     GemvFn fn = pick_mfma<true>(sh.H);
     if (!fn) return hipErrorInvalidValue;
     const int blocks = mfma_blocks(maxu, sh.I);
@@ -740,7 +776,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   a.code_off = sh.off_w2c;
   a.scale_off = sh.off_w2s;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
-  if (mfma && M >= kMfmaMinRows) {
+  if (mfma && M >= kMfmaMinRowsDown) {
     GemvFn fn = pick_mfma<false>(sh.I);
     if (!fn) return hipErrorInvalidValue;
     const int blocks = mfma_blocks(maxu, sh.H);

@@ -106,8 +106,16 @@ typedef struct {
  * order does not depend on how many rows share an expert) and the matrix-core
  * kernels, whose rounding differs, are not used.  Drafted and verify rows then
  * never change a row's output (the exact-decoding rule on the page "TensorFold
- * GLM-5.3 explained").  Costs speed at M >= 12. */
+ * GLM-5.3 explained").  Costs speed from M = 3 on (the matrix-core ranges
+ * below). */
 #define SC_FLAG_BATCH_INVARIANT 1u
+
+/* Without SC_FLAG_BATCH_INVARIANT, steps of at least this many rows run the
+ * gate/up (resp. down) product on the matrix cores; their rows need not be
+ * bit-equal to the same rows decoded alone (the outputs stay within the same
+ * tolerance of the exact result). */
+#define SC_MFMA_MIN_ROWS_GATEUP 13
+#define SC_MFMA_MIN_ROWS_DOWN 3
 
 typedef struct {
   size_t blob_bytes;              /* B_e */

@@ -80,3 +80,14 @@ def test_invalid_configs_are_rejected(kw, code):
         B.slotcache_query_sizes(_cfg(**kw))
     assert ei.value.status == code
     assert B.slotcache_last_error()
+
+
+def test_binding_constants_match_the_header():
+    """Every integer #define of include/slotcache.h that the binding mirrors has the same value."""
+    src = open(os.path.join(ROOT, "include", "slotcache.h")).read()
+    defs = dict(re.findall(r"^#define\s+(SC_\w+)\s+(\d+)u?\s*$", src, re.M))
+    mirrored = [n for n in defs if hasattr(B, n)]
+    assert {"SC_BYPASS_ROWS", "SC_FLAG_BATCH_INVARIANT", "SC_MFMA_MIN_ROWS_GATEUP",
+            "SC_MFMA_MIN_ROWS_DOWN", "SC_N_KERNELS"} <= set(mirrored)
+    for n in mirrored:
+        assert getattr(B, n) == int(defs[n]), n

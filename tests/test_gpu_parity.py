@@ -416,8 +416,9 @@ def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True):
 def test_batch_invariant_rows(shape):
     """SC_FLAG_BATCH_INVARIANT: every row of an M-row step (drafted rows sharing
     picks, M up to 16, and a prefill-sized bypass step) is bit-equal to the
-    same row decoded alone.  Without the flag the streaming kernels (M < 12)
-    are invariant too; the matrix-core kernels (M >= 12) need not be."""
+    same row decoded alone.  Without the flag the steps that run only the
+    streaming kernels (M below both matrix-core thresholds) are invariant too;
+    the matrix-core kernels need not be."""
     cfg = CONFIGS["tiny"]
     if shape == "glm32":
         g = CONFIGS["glm"]
@@ -431,8 +432,10 @@ def test_batch_invariant_rows(shape):
         sc.preload(0)
     Ms = [2, 3, 4, 8, 11, 12, 16, 24]
     bad_inv = _rows_vs_single(cfg, inv, one, Ms, seed=3)
-    bad_dflt = _rows_vs_single(cfg, dflt, one, [M for M in Ms if M < 12], seed=3)
-    log("rows differing from their one-row result: invariant %s; default (M < 12) %s" % (bad_inv, bad_dflt))
+    from hbm_expert_slot_amd import binding as B
+    m_stream = min(B.SC_MFMA_MIN_ROWS_GATEUP, B.SC_MFMA_MIN_ROWS_DOWN)
+    bad_dflt = _rows_vs_single(cfg, dflt, one, [M for M in Ms if M < m_stream], seed=3)
+    log("rows differing from their one-row result: invariant %s; default (M < %d) %s" % (bad_inv, m_stream, bad_dflt))
     assert all(v == 0 for v in bad_inv.values()), bad_inv
     assert all(v == 0 for v in bad_dflt.values()), bad_dflt
     assert inv.stats(0)["bypass_steps"] == 1      # M = 24 > 16
