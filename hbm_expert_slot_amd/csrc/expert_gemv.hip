@@ -380,17 +380,17 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 // Matrix-core path for steps with several rows per expert (draft / verify
-// batches).  One wavefront owns RT tiles of 16 output rows of one unique
-// expert and up to 16 of its picks; for every 128-wide K tile it decodes the
-// FP4 codes into bf16 pre-multiplied by their E4M3 block scale (exact: a code
-// has at most 2 significant bits and a scale 4, so the product fits bf16's 8)
-// and issues four v_mfma_f32_16x16x32_bf16.  Lane layout of that instruction
-// (checked on the device): A lane l = row l%16, k = 8*(l/16)+j; B lane l =
-// k = 8*(l/16)+j, column l%16; D lane l, j = row 4*(l/16)+j, column l%16.
-// Lane group g = l/16 therefore takes elements [32g, 32g+32) of the K tile --
-// one 16-byte code load and one 2-byte scale load -- and dword d of those
-// codes is its slice of the d-th MFMA.  The down projection's fp32 operand is
-// split into bf16 high and low parts (two MFMAs), keeping about 16 bits.
+// batches).  For every 128-wide K tile a wavefront decodes the FP4 codes of
+// 16 weight rows into bf16 pre-multiplied by their E4M3 block scale (exact: a
+// code has at most 2 significant bits and a scale 4, so the product fits
+// bf16's 8) and issues four v_mfma_f32_16x16x32_bf16 against up to 16 picks.
+// Lane layout of that instruction (checked on the device): A lane l = row
+// l%16, k = 8*(l/16)+j; B lane l = k = 8*(l/16)+j, column l%16; D lane l, j =
+// row 4*(l/16)+j, column l%16.  Lane group g = l/16 therefore takes elements
+// [32g, 32g+32) of the K tile -- 16 bytes of codes and 2 bytes of scales --
+// and dword d of those codes is its slice of the d-th MFMA.  The down
+// projection's fp32 operand is split into bf16 high and low parts (two
+// MFMAs), keeping about 16 bits.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
@@ -410,73 +410,122 @@ __device__ __forceinline__ bf16x8 bf16x8_from_words(const uint4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int K, bool GATEUP, int RT>
-struct GemvMfma {
-  static_assert(K % 128 == 0, "K must be a multiple of 128");
-  static constexpr int NKT = K / 128;
-  static constexpr int NM = GATEUP ? 2 : 1;
-  static constexpr int NX = GATEUP ? 4 : 8;     // 16-byte operand loads per lane and K tile
+// The weights are staged through LDS.  Loaded in the MFMA layout directly (16
+// rows x 64 bytes per instruction) they peaked at about 4.5 TB/s in a
+// pure-read test, against 6.8 TB/s for loads of whole cache lines.  A task is
+// 32 weight rows of one unique expert (gate/up: one 16-row tile of gate and
+// the matching tile of up; down: two 16-row tiles) against up to 16 of its
+// picks.  K is walked in stages of KC elements: the stage's 32 x KC/2 code
+// bytes are loaded row-contiguously (whole 128-byte lines per row) into
+// registers, written to the wavefront's LDS buffer and read back in the MFMA
+// lane layout while the next stage's loads are in flight.  In LDS, 16-byte
+// piece c of row j sits in slot c ^ (j mod PPR) of its row, so the 16 lanes of
+// one MFMA operand read (16 rows, one piece each) hit 16 different bank
+// groups.  The operand (x or h) slices come from global memory one K tile
+// ahead.  (Direct-to-LDS loads cannot be prefetched this way: the compiler
+// waits for all of them before any LDS read.)
+constexpr int kLdsStageK = 256;
 
-  // One K tile of a task: the codes and block scales of its RT row tiles (gate
-  // and up for gate/up) and the lane's pick-column operand slice.
-  struct Stage {
-    uint4 q[RT][NM];
-    uint32_t sc[RT][NM];
-    uint4 x[NX];
+template <int K, bool GATEUP>
+struct GemvMfmaL {
+  static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int RT = GATEUP ? 1 : 2;            // 16-row tiles per task
+  static constexpr int NROW = 16 * RT * NM;            // 32 weight rows
+  static constexpr int KC = K < kLdsStageK ? K : kLdsStageK;   // K elements per stage
+  static constexpr int NS = K / KC;                    // stages
+  static constexpr int PPR = KC / 32;                  // 16-byte code pieces per row and stage
+  static constexpr int CPL = NROW * PPR / 64;          // code pieces per lane and stage
+  static constexpr int SPR = KC / 64;                  // scale dwords per row and stage
+  static constexpr int SPL = NROW * SPR / 64;          // scale dwords per lane and stage
+  static constexpr int CODE_B = NROW * KC / 2;
+  static constexpr int STAGE_B = CODE_B + NROW * KC / 16;
+  static constexpr int NKT = KC / 128;                 // K tiles per stage
+  static constexpr int NX = GATEUP ? 4 : 8;            // 16-byte operand loads per lane and K tile
+  static_assert(K % KC == 0 && KC % 128 == 0 && CPL >= 1 && SPL >= 1, "unsupported K");
+  static_assert(NKT == 1 || NKT % 2 == 0, "operand double buffer assumes an even tile count per stage");
+
+  struct Regs {
+    uint4 c[CPL];
+    uint32_t s[SPL];
   };
 
-  // Every load is unconditional (no branches between the loads and their use,
-  // so the wait before a K tile's products covers that tile only): a ragged
-  // last task re-reads its last row tile for the tiles it does not have, and
-  // an idle pick column reads pick 0's operand row and zeroes it.
-  __device__ static __forceinline__ void load(Stage& st, const GemvArgs& a, const uint8_t* blob, int tile0, int nt,
-                                              const uint8_t* xsrc, bool live, int kt, int g, int n) {
+  // global row of task row j (a ragged task re-reads its last tile)
+  __device__ static __forceinline__ size_t grow(const GemvArgs& a, int tile0, int nt, int j) {
+    const int rt = j / (16 * NM), m = (j / 16) % NM, n = j % 16;
+    const int tile = tile0 + (rt < nt ? rt : nt - 1);
+    return (size_t)(tile * 16 + n + m * a.up_row0);
+  }
+
+  __device__ static __forceinline__ void gload(Regs& r, const GemvArgs& a, const uint8_t* blob, int tile0, int nt,
+                                               int stage, int lane) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int tile = tile0 + (rt < nt ? rt : nt - 1);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const size_t row = (size_t)(tile * 16 + n + m * a.up_row0);
-        st.q[rt][m] = ld16_stream(blob + a.code_off + row * (K / 2) + 64 * kt + 16 * g);
-        st.sc[rt][m] = ld2(blob + a.scale_off + row * (K / 16) + 8 * kt + 2 * g);
-      }
+    for (int i = 0; i < CPL; ++i) {
+      const int L = 64 * i + lane, j = L / PPR, slot = L % PPR;
+      const int c = slot ^ (j % PPR);
+      r.c[i] = ld16_stream(blob + a.code_off + grow(a, tile0, nt, j) * (K / 2) + stage * (KC / 2) + 16 * c);
     }
-    // elements [128 kt + 32 g, +32) of the pick's operand row (bf16 x or fp32 h)
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int D = 64 * i + lane, j = D / SPR, dw = D % SPR;
+      r.s[i] = *(const __attribute__((address_space(1))) uint32_t*)(blob + a.scale_off + grow(a, tile0, nt, j) * (K / 16) +
+                                                                   stage * (KC / 16) + 4 * dw);
+    }
+  }
+
+  __device__ static __forceinline__ void lstore(const Regs& r, uint8_t* buf, int lane) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int L = 64 * i + lane, j = L / PPR, slot = L % PPR;
+      *reinterpret_cast<uint4*>(buf + j * (KC / 2) + 16 * slot) = r.c[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int D = 64 * i + lane, j = D / SPR, dw = D % SPR;
+      *reinterpret_cast<uint32_t*>(buf + CODE_B + j * (KC / 16) + 4 * dw) = r.s[i];
+    }
+  }
+
+  // operand elements [128 kt + 32 g, +32) of the lane's pick (zero for an idle column)
+  __device__ static __forceinline__ void xload(uint4 (&x)[NX], const uint8_t* xsrc, bool live, int kt, int g) {
     const uint8_t* src = xsrc + (size_t)(128 * kt + 32 * g) * (GATEUP ? 2 : 4);
 #pragma unroll
     for (int v = 0; v < NX; ++v) {
       const uint4 t = ld16(src + 16 * v);
-      st.x[v] = make_uint4(live ? t.x : 0u, live ? t.y : 0u, live ? t.z : 0u, live ? t.w : 0u);
+      x[v] = make_uint4(live ? t.x : 0u, live ? t.y : 0u, live ? t.z : 0u, live ? t.w : 0u);
     }
   }
 
-  __device__ static __forceinline__ void compute(const Stage& st, f32x4 (&acc)[RT][NM]) {
-    // B operand: elements [128 kt + 32 g + 8 q, +8) of pick column n for MFMA q
+  // the products of K tile kt' of the stage in buf
+  __device__ static __forceinline__ void tile(const uint8_t* buf, int ktp, const uint4 (&x)[NX], f32x4 (&acc)[RT][NM],
+                                              int g, int n) {
     bf16x8 bh[4], bl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (GATEUP) {
-        bh[q] = bf16x8_from_words(st.x[q]);
+        bh[q] = bf16x8_from_words(x[q]);
       } else {
-        const uint4 w0 = st.x[2 * q], w1 = st.x[2 * q + 1];
+        const uint4 w0 = x[2 * q], w1 = x[2 * q + 1];
         const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float hv = __uint_as_float(wv[j]);
+        for (int e = 0; e < 8; ++e) {
+          const float hv = __uint_as_float(wv[e]);
           const __bf16 hi = (__bf16)hv;
-          bh[q][j] = hi;
-          bl[q][j] = (__bf16)(hv - (float)hi);
+          bh[q][e] = hi;
+          bl[q][e] = (__bf16)(hv - (float)hi);
         }
       }
     }
-    // all RT tiles (a ragged task's extra tiles are computed and not stored)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const float s0 = __builtin_amdgcn_cvt_f32_fp8(st.sc[rt][m], 0);
-        const float s1 = __builtin_amdgcn_cvt_f32_fp8(st.sc[rt][m], 1);
-        const uint32_t d[4] = {st.q[rt][m].x, st.q[rt][m].y, st.q[rt][m].z, st.q[rt][m].w};
+        const int j = (rt * NM + m) * 16 + n;
+        const int slot = (4 * ktp + g) ^ (j % PPR);
+        const uint4 q4 = *reinterpret_cast<const uint4*>(buf + j * (KC / 2) + 16 * slot);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(buf + CODE_B + j * (KC / 16) + 8 * ktp + 2 * g);
+        const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+        const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
+        const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bf16x8 av = fp4x8_scaled_bf16(d[q], q < 2 ? s0 : s1);
@@ -487,13 +536,24 @@ struct GemvMfma {
     }
   }
 
-  __device__ static __forceinline__ void run(const GemvArgs& a) {
+  // LDS writes of this wavefront are complete and ordered before its later reads
+  __device__ static __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  __device__ static __forceinline__ void run(const GemvArgs& a, uint8_t* lds) {
     int lo, U;
     launch_uniques(a, a.hdr[H_UNIQUE], lo, U);
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, n = lane & 15;
     const int nwaves = gridDim.x * (kGemvThreads / 64);
-    const int gw = blockIdx.x * (kGemvThreads / 64) + wave_id();
+    const int w = wave_id();
+    const int gw = blockIdx.x * (kGemvThreads / 64) + w;
+    uint8_t* buf0 = lds + (size_t)w * 2 * STAGE_B;
+    uint8_t* buf1 = buf0 + STAGE_B;
     const int ntiles = a.rows / 16;
     const int tpu = (ntiles + RT - 1) / RT;     // tasks per unique expert
     const int ntask = U * tpu;
@@ -515,17 +575,37 @@ struct GemvMfma {
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        // K tiles with the next tile's loads in flight while the current one is multiplied
-        Stage A, B;
-        load(A, a, blob, tile0, nt, xsrc, live, 0, g, n);
-        int kt = 0;
-        while (true) {
-          if (kt + 1 < NKT) load(B, a, blob, tile0, nt, xsrc, live, kt + 1, g, n);
-          compute(A, acc);
-          if (++kt >= NKT) break;
-          if (kt + 1 < NKT) load(A, a, blob, tile0, nt, xsrc, live, kt + 1, g, n);
-          compute(B, acc);
-          if (++kt >= NKT) break;
+        Regs R;
+        uint4 xa[NX], xb[NX];
+        gload(R, a, blob, tile0, nt, 0, lane);
+        xload(xa, xsrc, live, 0, g);
+        lstore(R, buf0, lane);
+        if (NS > 1) gload(R, a, blob, tile0, nt, 1, lane);
+        lds_sync();
+        for (int st = 0; st < NS; ++st) {
+          const uint8_t* cur = (st & 1) ? buf1 : buf0;
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) {
+            const int kt = st * NKT + ktp;
+            // even tiles use xa, odd ones xb; the next tile's operand loads go to the other
+            if ((ktp & 1) == 0) {
+              if (kt + 1 < NS * NKT) xload(xb, xsrc, live, kt + 1, g);
+              tile(cur, ktp, xa, acc, g, n);
+            } else {
+              if (kt + 1 < NS * NKT) xload(xa, xsrc, live, kt + 1, g);
+              tile(cur, ktp, xb, acc, g, n);
+            }
+          }
+          if (NKT == 1) {
+            // one tile per stage: the next stage's operand is in xb; move it to xa
+#pragma unroll
+            for (int v = 0; v < NX; ++v) xa[v] = xb[v];
+          }
+          if (st + 1 < NS) {
+            lstore(R, (st & 1) ? buf0 : buf1, lane);
+            if (st + 2 < NS) gload(R, a, blob, tile0, nt, st + 2, lane);
+            lds_sync();
+          }
         }
         if (live) {
 #pragma unroll
@@ -535,22 +615,29 @@ struct GemvMfma {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               v[j] = GATEUP ? silu_f32(acc[rt][0][j] * gs) * (acc[rt][NM - 1][j] * gs) : acc[rt][0][j] * gs;
-            // rows 16 tile + 4 g .. + 3 of pick p: one 16-byte store
             *reinterpret_cast<float4*>(a.out + (size_t)p * a.rows + (tile0 + rt) * 16 + 4 * g) =
                 make_float4(v[0], v[1], v[2], v[3]);
           }
         }
+        // the next task's first stage overwrites buf0, which this one may still be reading
+        lds_sync();
       }
     }
   }
 };
 
-template <int K, bool GATEUP, int RT>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma(GemvArgs a) {
+// LDS of the staged kernel: two stage buffers per wavefront.
+template <int K, bool GATEUP>
+constexpr int mfma_lds_bytes() { return (kGemvThreads / 64) * 2 * GemvMfmaL<K, GATEUP>::STAGE_B; }
+
+template <int K, bool GATEUP>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma_lds(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<K, GATEUP>()];
   span_start(a.span);
-  GemvMfma<K, GATEUP, RT>::run(a);
+  GemvMfmaL<K, GATEUP>::run(a, lds);
   span_end(a.span);
 }
+
 
 // Copies the step's missed blobs (host-mapped pinned memory -> HBM slots), or
 // one group of a staged prefill step's experts into the staging blobs (group
@@ -680,34 +767,35 @@ int mr_for(int M) { return M == 1 ? 1 : 2; }
 
 // Rows per step from which each product runs on the matrix cores (all-hit GLM
 // layer, drafted rows, µs per kernel, streaming against matrix cores): gate/up
-// 141 / 160 at M = 8, 212 / 219 at 12, 268 / 232 at 14; down 39 / 46 at M = 2,
-// 62 / 50 at 3.  The two-pick streaming down kernel holds about 480 VGPRs (one
-// wavefront per SIMD), the matrix-core one about 180.
+// 77 / 81 at M = 4, 110 / 84 at 6, 141 / 101 at 8; down 39 / 39 at M = 2,
+// 62 / 41 at 3.  The two-pick streaming down kernel holds about 480 VGPRs (one
+// wavefront per SIMD).
 constexpr int kMfmaMinRowsGateup = SC_MFMA_MIN_ROWS_GATEUP;
 constexpr int kMfmaMinRowsDown = SC_MFMA_MIN_ROWS_DOWN;
-constexpr int kMfmaTiles = 2;     // 16-row tiles per wavefront task (measured against 1 and 4)
 
 template <bool GATEUP>
 GemvFn pick_mfma(int K) {
   switch (K) {
-    case 128: return GATEUP ? nullptr : k_gemv_mfma<128, GATEUP, kMfmaTiles>;
-    case 256: return k_gemv_mfma<256, GATEUP, kMfmaTiles>;
-    case 512: return k_gemv_mfma<512, GATEUP, kMfmaTiles>;
-    case 1024: return k_gemv_mfma<1024, GATEUP, kMfmaTiles>;
-    case 2048: return k_gemv_mfma<2048, GATEUP, kMfmaTiles>;
-    case 4096: return k_gemv_mfma<4096, GATEUP, kMfmaTiles>;
-    case 6144: return k_gemv_mfma<6144, GATEUP, kMfmaTiles>;
-    case 8192: return k_gemv_mfma<8192, GATEUP, kMfmaTiles>;
+    case 128: return GATEUP ? nullptr : k_gemv_mfma_lds<128, GATEUP>;
+    case 256: return k_gemv_mfma_lds<256, GATEUP>;
+    case 512: return k_gemv_mfma_lds<512, GATEUP>;
+    case 1024: return k_gemv_mfma_lds<1024, GATEUP>;
+    case 2048: return k_gemv_mfma_lds<2048, GATEUP>;
+    case 4096: return k_gemv_mfma_lds<4096, GATEUP>;
+    case 6144: return k_gemv_mfma_lds<6144, GATEUP>;
+    case 8192: return k_gemv_mfma_lds<8192, GATEUP>;
     default: return nullptr;
   }
 }
 
-// One wavefront per task, at most 1024 blocks.
-int mfma_blocks(long maxu, int rows) {
-  const long tasks = maxu * ((rows / 16 + kMfmaTiles - 1) / kMfmaTiles);
+// One wavefront per task (32 weight rows of one expert), at most cap blocks.
+constexpr int kMfmaBlocksGateup = 768;
+constexpr int kMfmaBlocksDown = 512;
+int mfma_blocks(long maxu, int rows, int cap) {
+  const long tasks = maxu * (rows / 32 > 0 ? rows / 32 : 1);
   long blocks = (tasks + 3) / 4;
   if (blocks < 1) blocks = 1;
-  if (blocks > 1024) blocks = 1024;
+  if (blocks > cap) blocks = cap;
   return (int)blocks;
 }
 
@@ -752,7 +840,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   if (mfma && M >= kMfmaMinRowsGateup) {
     GemvFn fn = pick_mfma<true>(sh.H);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.I);
+    const int blocks = mfma_blocks(maxu, sh.I, kMfmaBlocksGateup);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
@@ -779,7 +867,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   if (mfma && M >= kMfmaMinRowsDown) {
     GemvFn fn = pick_mfma<false>(sh.I);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.H);
+    const int blocks = mfma_blocks(maxu, sh.H, kMfmaBlocksDown);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
