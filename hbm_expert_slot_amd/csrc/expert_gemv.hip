@@ -44,11 +44,12 @@ struct GemvArgs {
   const float* gs;       // [E][2] global scales of the layer's bank
   const int32_t* uniq_off;
   const int32_t* uniq_picks;
-  const void* operand;   // gate/up: bf16 x [M][H]; down: fp32 h [P][I]
+  const void* operand;   // gate/up: bf16 x [M][H]; down: h [P][I], 4 bytes per element
   float* out;            // gate/up: h [P][I];      down: part [P][H]
   int rows;              // output rows per expert: I (gate/up) or H (down)
   int k;                 // top-k: pick p belongs to row p / k
   int up_row0;           // gate/up: first up row (I)
+  int split_h;           // gate/up: write h split for the matrix-core down product (see store_h)
   int64_t code_off;      // offset of the code rows inside a blob
   int64_t scale_off;     // offset of the scale rows inside a blob
   uint64_t* span;        // execution stamps of a timed step, else null
@@ -74,6 +75,25 @@ __device__ __forceinline__ int unique_at(const GemvArgs& a, int lo, int j) {
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// h as the matrix-core down product reads it: each group of 8 elements is 16
+// bytes of bf16 high parts then 16 bytes of bf16 low parts (hi = bf16(v), lo =
+// bf16(v - hi)), so a pick's row keeps the 4 bytes per element of fp32 h.
+__device__ __forceinline__ void split_bf16(float v, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)v;
+  lo = (__bf16)(v - (float)hi);
+}
+__device__ __forceinline__ void store_h(float* row, int r, float v, bool split) {
+  if (!split) {
+    row[r] = v;
+    return;
+  }
+  __bf16 hi, lo;
+  split_bf16(v, hi, lo);
+  __bf16* grp = reinterpret_cast<__bf16*>(row) + (r / 8) * 16 + (r % 8);
+  grp[0] = hi;
+  grp[8] = lo;
+}
 
 // Loads through global-address-space pointers: blob pointers come from memory,
 // so without the cast the compiler emits flat loads (which also count against
@@ -282,8 +302,11 @@ struct Gemv {
         for (int mi = 0; mi < MR; ++mi) {
           if (idx == j * MR + mi && mi < nc && i + j < n) {
             const int r = (base + (i + j) * stride) * RPW + rsub;
-            a.out[(size_t)pk[mi] * a.rows + r] =
-                GATEUP ? silu_f32(v0[0] * gs) * (v1[0] * gs) : v0[0] * gs;
+            if (GATEUP)
+              store_h(a.out + (size_t)pk[mi] * a.rows, r, silu_f32(v0[0] * gs) * (v1[0] * gs),
+                      !SINGLE && a.split_h);   // one-row steps never run the matrix cores
+            else
+              a.out[(size_t)pk[mi] * a.rows + r] = v0[0] * gs;
           }
         }
       }
@@ -392,6 +415,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
 // projection's fp32 operand is split into bf16 high and low parts (two
 // MFMAs), keeping about 16 bits.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t c, float s) {
@@ -504,15 +528,9 @@ struct GemvMfmaL {
       if (GATEUP) {
         bh[q] = bf16x8_from_words(x[q]);
       } else {
-        const uint4 w0 = x[2 * q], w1 = x[2 * q + 1];
-        const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float hv = __uint_as_float(wv[e]);
-          const __bf16 hi = (__bf16)hv;
-          bh[q][e] = hi;
-          bl[q][e] = (__bf16)(hv - (float)hi);
-        }
+        // h arrives split (store_h): 8 high parts, then their 8 low parts
+        bh[q] = bf16x8_from_words(x[2 * q]);
+        bl[q] = bf16x8_from_words(x[2 * q + 1]);
       }
     }
 #pragma unroll
@@ -615,8 +633,23 @@ struct GemvMfmaL {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               v[j] = GATEUP ? silu_f32(acc[rt][0][j] * gs) * (acc[rt][NM - 1][j] * gs) : acc[rt][0][j] * gs;
-            *reinterpret_cast<float4*>(a.out + (size_t)p * a.rows + (tile0 + rt) * 16 + 4 * g) =
-                make_float4(v[0], v[1], v[2], v[3]);
+            const int r0 = (tile0 + rt) * 16 + 4 * g;      // r0 % 8 is 0 or 4
+            float* row = a.out + (size_t)p * a.rows;
+            if (GATEUP && a.split_h) {
+              bf16x4 hi, lo;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                __bf16 h, l;
+                split_bf16(v[j], h, l);
+                hi[j] = h;
+                lo[j] = l;
+              }
+              __bf16* grp = reinterpret_cast<__bf16*>(row) + (r0 / 8) * 16 + (r0 % 8);
+              *reinterpret_cast<bf16x4*>(grp) = hi;
+              *reinterpret_cast<bf16x4*>(grp + 8) = lo;
+            } else {
+              *reinterpret_cast<float4*>(row + r0) = make_float4(v[0], v[1], v[2], v[3]);
+            }
           }
         }
         // the next task's first stage overwrites buf0, which this one may still be reading
@@ -823,6 +856,7 @@ static GemvArgs base_args(const Workspace& W, const float* gs, int group) {
   a.order = W.uniq_order;
   a.group = group;
   a.G = W.stage_n;
+  a.split_h = 0;
   return a;
 }
 
@@ -836,6 +870,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.up_row0 = sh.I;
   a.code_off = 0;
   a.scale_off = sh.off_w13s;
+  a.split_h = mfma && M >= kMfmaMinRowsDown;   // the down product of this step runs on the matrix cores
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (mfma && M >= kMfmaMinRowsGateup) {
     GemvFn fn = pick_mfma<true>(sh.H);
