@@ -450,11 +450,10 @@ __device__ __forceinline__ bf16x8 bf16x8_from_words(const uint4& v) {
 // waits for all of them before any LDS read.)
 constexpr int kLdsStageK = 256;
 
-template <int K, bool GATEUP>
+template <int K, bool GATEUP, int RT>
 struct GemvMfmaL {
   static constexpr int NM = GATEUP ? 2 : 1;
-  static constexpr int RT = GATEUP ? 1 : 2;            // 16-row tiles per task
-  static constexpr int NROW = 16 * RT * NM;            // 32 weight rows
+  static constexpr int NROW = 16 * RT * NM;            // weight rows per task
   static constexpr int KC = K < kLdsStageK ? K : kLdsStageK;   // K elements per stage
   static constexpr int NS = K / KC;                    // stages
   static constexpr int PPR = KC / 32;                  // 16-byte code pieces per row and stage
@@ -659,15 +658,26 @@ struct GemvMfmaL {
   }
 };
 
+// 16-row tiles per task: 32 weight rows for gate/up (a gate tile and its up
+// tile), 64 for down.  Each task reloads its picks' operand slices from L2
+// for every K tile, so larger tasks cut that traffic per weight byte; at 64
+// rows the down kernel holds about 270 registers (one wavefront per SIMD) and
+// is still faster than at 32 (GLM layer, M = 16: 91 against 105 us); 64-row
+// gate/up tasks gained nothing.
+constexpr int kMfmaTilesGateup = 1;
+constexpr int kMfmaTilesDown = 4;
+template <bool GATEUP>
+constexpr int mfma_tiles() { return GATEUP ? kMfmaTilesGateup : kMfmaTilesDown; }
+
 // LDS of the staged kernel: two stage buffers per wavefront.
 template <int K, bool GATEUP>
-constexpr int mfma_lds_bytes() { return (kGemvThreads / 64) * 2 * GemvMfmaL<K, GATEUP>::STAGE_B; }
+constexpr int mfma_lds_bytes() { return (kGemvThreads / 64) * 2 * GemvMfmaL<K, GATEUP, mfma_tiles<GATEUP>()>::STAGE_B; }
 
 template <int K, bool GATEUP>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma_lds(GemvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<K, GATEUP>()];
   span_start(a.span);
-  GemvMfmaL<K, GATEUP>::run(a, lds);
+  GemvMfmaL<K, GATEUP, mfma_tiles<GATEUP>()>::run(a, lds);
   span_end(a.span);
 }
 
@@ -821,11 +831,11 @@ GemvFn pick_mfma(int K) {
   }
 }
 
-// One wavefront per task (32 weight rows of one expert), at most cap blocks.
+// One wavefront per task (RT 16-row tiles of one expert), at most cap blocks.
 constexpr int kMfmaBlocksGateup = 768;
 constexpr int kMfmaBlocksDown = 512;
-int mfma_blocks(long maxu, int rows, int cap) {
-  const long tasks = maxu * (rows / 32 > 0 ? rows / 32 : 1);
+int mfma_blocks(long maxu, int rows, int rt, int cap) {
+  const long tasks = maxu * ((rows / 16 + rt - 1) / rt);
   long blocks = (tasks + 3) / 4;
   if (blocks < 1) blocks = 1;
   if (blocks > cap) blocks = cap;
@@ -875,7 +885,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   if (mfma && M >= kMfmaMinRowsGateup) {
     GemvFn fn = pick_mfma<true>(sh.H);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.I, kMfmaBlocksGateup);
+    const int blocks = mfma_blocks(maxu, sh.I, kMfmaTilesGateup, kMfmaBlocksGateup);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
@@ -902,7 +912,7 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   if (mfma && M >= kMfmaMinRowsDown) {
     GemvFn fn = pick_mfma<false>(sh.I);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.H, kMfmaBlocksDown);
+    const int blocks = mfma_blocks(maxu, sh.H, kMfmaTilesDown, kMfmaBlocksDown);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
