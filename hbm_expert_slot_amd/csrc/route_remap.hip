@@ -183,14 +183,24 @@ struct RouteArgs {
 // l, l+64, ... sorted by (logit descending, id ascending).  Each round takes
 // the wavefront maximum of the lanes' head order words (32-bit); equal heads
 // are settled by the lowest expert id, and the owner lane pops its head.
-// Lane j < k returns the j-th pick and its logit.
+// Lane j < k returns the j-th pick and its logit.  z holds the lane's
+// logits (load_row).
 template <int EPL>
-__device__ __forceinline__ void route_row(const float* z, int E, int k, int lane, int* pick, float* logit) {
+__device__ __forceinline__ void load_row(const float* row, int E, int lane, float (&z)[EPL]) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    z[i] = e < E ? row[e] : 0.0f;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_row(const float (&z)[EPL], int E, int k, int lane, int* pick, float* logit) {
   uint64_t keys[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    keys[i] = e < E ? order_key(z[e], e) : 0ull;
+    keys[i] = e < E ? order_key(z[i], e) : 0ull;
   }
 #pragma unroll
   for (int i = 1; i < EPL; ++i)
@@ -233,7 +243,8 @@ __device__ __forceinline__ void route_row(const float* z, int E, int k, int lane
 template <int EPL>
 __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   constexpr int SPT = kMaxSlots / kRouteThreads;   // slots per thread
-  __shared__ int s_pick[kMaxPicks];
+  constexpr int XPT = kMaxExperts / kRouteThreads; // experts per thread
+  __shared__ __attribute__((aligned(16))) int s_pick[kMaxPicks];
   __shared__ int s_first[kMaxExperts];   // first pick position per expert; later pick counts
   __shared__ int s_last[kMaxExperts];
   __shared__ int s_uidx[kMaxExperts];
@@ -262,46 +273,80 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     for (int c = 0; c < C_N; ++c) cnt[c] = a.L.counters[c];
   }
 
-  // Snapshot the layer state into LDS; these loads overlap the logits loads.
-  for (int e = tid; e < E; e += kRouteThreads) {
-    s_e2s[e] = a.L.e2s[e];
-    s_first[e] = INT_MAX;
-    s_last[e] = -1;
+  // Layer state and the first logits rows are loaded up front; the state
+  // goes to LDS once the rows are routed, so the two latencies overlap.
+  int r_e2s[XPT], r_s2e[SPT];
+  int64_t r_key[SPT];
+#pragma unroll
+  for (int q = 0; q < XPT; ++q) {
+    const int e = tid + q * kRouteThreads;
+    r_e2s[q] = e < E ? a.L.e2s[e] : -1;
   }
-  for (int sl = tid; sl < S; sl += kRouteThreads) {
-    s_s2e[sl] = a.L.s2e[sl];
-    s_key[sl] = (long long)a.L.key[sl];
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sl = tid + q * kRouteThreads;
+    r_s2e[q] = sl < S ? a.L.s2e[sl] : -1;
+    r_key[q] = sl < S ? a.L.key[sl] : -1;
+  }
+
+  // ---- router: one row per wavefront, up to four rows' logits in flight ----
+  constexpr int NW = kRouteThreads / 64;
+  constexpr int RD = 4;                         // rows in flight per wavefront
+  float zr[RD][EPL];
+#pragma unroll
+  for (int d = 0; d < RD; ++d)
+    if (wave + d * NW < M) load_row<EPL>(a.logits + (size_t)(wave + d * NW) * E, E, lane, zr[d]);
+  for (int m0 = wave; m0 < M; m0 += RD * NW) {
+#pragma unroll
+    for (int d = 0; d < RD; ++d) {
+      const int m = m0 + d * NW;
+      if (m >= M) break;
+      int my_e;
+      float zj;
+      route_row<EPL>(zr[d], E, k, lane, &my_e, &zj);
+      if (m + RD * NW < M) load_row<EPL>(a.logits + (size_t)(m + RD * NW) * E, E, lane, zr[d]);
+      // weights: softmax over the k chosen logits (limits for non-finite picks)
+      const bool act = lane < k;
+      if (!act) zj = 0.0f;
+      const bool is_nan = zj != zj;
+      const bool pinf = act && zj == INFINITY;
+      const int npinf = __popcll(__ballot(pinf));
+      const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
+      float w;
+      if (npinf > 0) {
+        w = pinf ? 1.0f / (float)npinf : 0.0f;
+      } else if (z0 != z0 || z0 == -INFINITY) {
+        w = 1.0f / (float)k;
+      } else {
+        const float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
+        const float sum = wave_sum_f32(ex);
+        w = ex / sum;
+      }
+      if (act) {
+        s_pick[m * k + lane] = my_e;
+        a.W.pick_expert[m * k + lane] = my_e;
+        a.W.pick_w[m * k + lane] = w;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < XPT; ++q) {
+    const int e = tid + q * kRouteThreads;
+    if (e < E) {
+      s_e2s[e] = r_e2s[q];
+      s_first[e] = INT_MAX;
+      s_last[e] = -1;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int sl = tid + q * kRouteThreads;
+    if (sl < S) {
+      s_s2e[sl] = r_s2e[q];
+      s_key[sl] = (long long)r_key[q];
+    }
   }
   if (tid == 0) s_nevict = 0;
-
-  // ---- router: one row per wavefront -------------------------------------
-  for (int m = wave; m < M; m += kRouteThreads / 64) {
-    int my_e;
-    float zj;
-    route_row<EPL>(a.logits + (size_t)m * E, E, k, lane, &my_e, &zj);
-    // weights: softmax over the k chosen logits (limits for non-finite picks)
-    const bool act = lane < k;
-    if (!act) zj = 0.0f;
-    const bool is_nan = zj != zj;
-    const bool pinf = act && zj == INFINITY;
-    const int npinf = __popcll(__ballot(pinf));
-    const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
-    float w;
-    if (npinf > 0) {
-      w = pinf ? 1.0f / (float)npinf : 0.0f;
-    } else if (z0 != z0 || z0 == -INFINITY) {
-      w = 1.0f / (float)k;
-    } else {
-      const float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
-      const float sum = wave_sum_f32(ex);
-      w = ex / sum;
-    }
-    if (act) {
-      s_pick[m * k + lane] = my_e;
-      a.W.pick_expert[m * k + lane] = my_e;
-      a.W.pick_w[m * k + lane] = w;
-    }
-  }
   __syncthreads();
 
   // ---- unique experts in first-occurrence order ----------------------------
@@ -504,8 +549,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     block_scan(s_cnt, s_off, U, s_wc);
     for (int p = tid; p < P; p += kRouteThreads) {
       const int e = s_pick[p];
-      int r = 0;
-      for (int q = 0; q < p; ++q) r += s_pick[q] == e;
+      // rank of p among the picks of e: earlier picks of e, four per LDS read
+      int r = 0, q = 0;
+      const int4* pk4 = reinterpret_cast<const int4*>(s_pick);
+      for (; q + 4 <= p; q += 4) {
+        const int4 v = pk4[q >> 2];
+        r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+      }
+      for (; q < p; ++q) r += s_pick[q] == e;
       a.W.uniq_picks[s_off[s_uidx[e]] + r] = p;
     }
     for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_off[u] = s_off[u];
