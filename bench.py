@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--sweep-rows", default="",
                     help="comma-separated M values: all-hit GLM layer (every expert resident), drafted rows; "
                          "prints one JSON line per M instead of the headline line")
+    ap.add_argument("--no-drafted", action="store_true",
+                    help="skip the drafted-rows workload (GLM layer, M = 4 / 16 / 64 schedule) in the default run")
     ap.add_argument("--prefill", action="store_true",
                     help="only time M=64 prefill chunks on the GLM layer (128 slots warmed by 64 one-row steps), "
                          "staged 64 experts at a time and read in place; prints one JSON line")
@@ -258,6 +260,67 @@ def prefill(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scal
     print(json.dumps(out), flush=True)
 
 
+def drafted_workload(torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace, no_flush):
+    """The drafted-rows workload on the GLM layer with 128 slots: 4-row draft rounds, a 16-row verify
+    step every 10th step and a 64-row prefill chunk (staged, 64 experts per group) every 50th; after 32
+    warm-up steps, one HIP-graph replay of the next 200 steps (each after the cache sweep) minus a replay
+    of the sweeps alone."""
+    cfg = CONFIGS["glm_draft"]
+    dev = torch.device("cuda:0")
+    W, K = 32, 200
+    logits, rows = routing_trace(cfg, 0, steps=W + K)
+    rows = [int(r) for r in rows]
+    Mmax = max(rows)
+    sc = SlotCache(1, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.slots, Mmax)
+    expert_blobs(cfg, 0, out=sc.backing(0))
+    sc.set_global_scales(0, global_scales(cfg, 0, "unit"))
+    d_l = [torch.from_numpy(logits[t, :rows[t]].copy()).to(dev) for t in range(W + K)]
+    d_x = [torch.from_numpy(activations(cfg, 0, t, rows[t]).view(np.int16)).to(dev) for t in range(W + K)]
+    y = torch.empty((Mmax, cfg.hidden), dtype=torch.float32, device=dev)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    for t in range(W):
+        sc.decode(0, d_l[t], d_x[t], y[:rows[t]])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    gstream = torch.cuda.Stream(dev)
+    graphs = []
+    for with_steps in (True, False):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            g.capture_begin()
+            for t in range(W, W + K):
+                if not no_flush:
+                    sink.copy_(flush.amax())
+                if with_steps:
+                    sc.decode(0, d_l[t], d_x[t], y[:rows[t]], stream=gstream)
+            g.capture_end()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graphs[1].replay()
+    torch.cuda.synchronize()
+    ms = []
+    st0 = sc.stats(0)
+    for g in graphs:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    st1 = sc.stats(0)
+    sc.close()
+    d = {n: st1[n] - st0[n] for n in ("steps", "bypass_steps", "lookups", "hits", "misses", "bypass_bytes")}
+    counts = {str(m): rows[W:].count(m) for m in sorted(set(rows[W:]))}
+    return {"workload": "GLM layer, 128 slots, drafted rows: M per step %s over %d steps after %d warm-up steps"
+                        % (counts, K, W),
+            "us_per_layer_step": round((ms[0] - (0.0 if no_flush else ms[1])) * 1e3 / K, 2),
+            "hit_rate_cached_steps": round(d["hits"] / d["lookups"], 4) if d["lookups"] else None,
+            "misses": d["misses"], "bypass_steps": d["bypass_steps"],
+            "bypass_host_GB": round(d["bypass_bytes"] / 1e9, 3),
+            "timing": "one HIP-graph replay of the steps (each after the cache sweep) minus a replay of the sweeps alone"}
+
+
 def main():
     a = parse()
     if a.trace_summary:
@@ -455,10 +518,14 @@ def main():
         "token_model": {"n_moe_layers": 75, "us_per_layer_step": round(graph_us, 3), "other_ms": 3.0,
                         "tok_per_s": round(1000.0 / (75 * graph_us / 1000.0 + 3.0), 2)},
     }
+    sc.close()
+    if not a.no_drafted and a.config == "glm":
+        print("bench: drafted-rows workload (M = 4 / 16 / 64 schedule)", file=sys.stderr, flush=True)
+        result["drafted_workload"] = drafted_workload(torch, SlotCache, CONFIGS, activations, expert_blobs,
+                                                      global_scales, routing_trace, a.no_flush)
     if not a.no_cpu_baseline:
         print("bench: timing the oracle on a bounded CPU sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, logits, xs, W, a.cpu_baseline_steps)
-    sc.close()
     print(json.dumps(result))
 
 
