@@ -229,7 +229,7 @@ struct XRed {
 // kernel takes U from the launch instead of the header and skips the CSR
 // lookups, so a wavefront's first weight loads wait for one pointer load only
 // and its activation loads for none.
-template <int K, int MR, int R, bool GATEUP, bool STRIDED, bool SINGLE = false>
+template <int K, int MR, int R, bool GATEUP, bool SINGLE = false>
 struct Gemv {
   using G = Geo<K>;
   static constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
@@ -333,16 +333,8 @@ struct Gemv {
       const int j = task / wpu, sub = task - (task / wpu) * wpu;
       const int u = SINGLE ? j : unique_at(a, lo, j);
       // a task owns row steps base + i * stride, i < n
-      int base, stride, n;
-      if (STRIDED) {
-        base = sub;
-        stride = wpu;
-        n = (spu - sub + wpu - 1) / wpu;
-      } else {
-        base = sub * q + (sub < rem ? sub : rem);
-        stride = 1;
-        n = q + (sub < rem ? 1 : 0);
-      }
+      const int base = sub * q + (sub < rem ? sub : rem), stride = 1;
+      const int n = q + (sub < rem ? 1 : 0);
       if (n <= 0) continue;
       const uint8_t* blob = a.uniq_ptr[u];
       const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
@@ -394,10 +386,10 @@ struct Gemv {
   }
 };
 
-template <int K, int MR, int R, bool GATEUP, bool STRIDED, bool SINGLE>
+template <int K, int MR, int R, bool GATEUP, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   span_start(a.span);
-  Gemv<K, MR, R, GATEUP, STRIDED, SINGLE>::run(a);
+  Gemv<K, MR, R, GATEUP, SINGLE>::run(a);
   span_end(a.span);
 }
 
@@ -760,7 +752,7 @@ constexpr int stage_rows() {
 
 template <int K, int MR, bool GATEUP, bool SINGLE>
 GemvFn gemv_fn() {
-  return k_gemv<K, MR, stage_rows<K, MR, GATEUP>(), GATEUP, false, SINGLE>;
+  return k_gemv<K, MR, stage_rows<K, MR, GATEUP>(), GATEUP, SINGLE>;
 }
 
 // MR = 0 selects the one-row variant (one pick per expert, U = k).
