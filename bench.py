@@ -28,7 +28,7 @@ METRIC = "µs per MoE layer-step (M=1) + achieved HBM GB/s vs peak; LRU hit rate
 HBM_PEAK_GBS = 8000.0
 PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16, per direction
 PHASES = ("route_remap", "fill", "gateup", "down", "combine")
-KERNEL_NAMES = {"gateup": "k_gemv<6144, 1, 1, true, true>", "down": "k_gemv<2048, 1, 8, false, true>"}
+KERNEL_NAMES = {"gateup": "k_gemv<6144, 1, 1, true, true>", "down": "k_gemv<2048, 1, 4, false, true>"}
 
 
 def parse():

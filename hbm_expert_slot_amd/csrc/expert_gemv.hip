@@ -243,25 +243,24 @@ struct Gemv {
     uint32_t sc[R][NM][NSEG];
   };
 
-  // Row step of the task's i-th step: base + i * stride.
+  // Row step of the task's i-th step: base + i * stride.  The loads carry no
+  // branches, so the wait before a stage's products covers that stage only
+  // (with one branch per row the compiler waited for every outstanding load,
+  // the next stage's included): a stage past the end of the run re-reads the
+  // run's last row step, and process() stores nothing for it.
   __device__ static __forceinline__ void load(Buf& b, const uint8_t* code_base, const uint8_t* scale_base,
                                               int i, int n, int base, int stride, int rsub, int up_row0) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const bool ok = i + j < n;
-      const int r = (base + (i + j) * stride) * RPW + rsub;
+      const int step = i + j < n ? i + j : n - 1;
+      const int r = (base + step * stride) * RPW + rsub;
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const size_t row = (size_t)(r + m * up_row0);
 #pragma unroll
         for (int c = 0; c < NSEG; ++c) {
-          if (ok) {
-            b.q[j][m][c] = ld16_stream(code_base + row * (K / 2) + c * 1024);
-            b.sc[j][m][c] = ld2(scale_base + row * (K / 16) + c * 128);
-          } else {
-            b.q[j][m][c] = make_uint4(0u, 0u, 0u, 0u);
-            b.sc[j][m][c] = 0u;
-          }
+          b.q[j][m][c] = ld16_stream(code_base + row * (K / 2) + c * 1024);
+          b.sc[j][m][c] = ld2(scale_base + row * (K / 16) + c * 128);
         }
       }
     }
@@ -742,11 +741,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* part, const float*
 
 typedef void (*GemvFn)(GemvArgs);
 
-// Row steps per pipeline stage: as many as the row group can reduce at once, at most 8 for down, 1 for gate/up.
+// Row steps per pipeline stage: as many as the row group can reduce at once, at most 4 for down (measured
+// against 2 and 8 on the GLM layer at M = 1: 12.7 against 13.6 and 13.3 us), 1 for gate/up.
 template <int K, int MR, bool GATEUP>
 constexpr int stage_rows() {
   constexpr int lim = Geo<K>::LPR / MR;
-  constexpr int want = GATEUP ? 1 : 8;
+  constexpr int want = GATEUP ? 1 : 4;
   return want < lim ? want : lim;
 }
 
@@ -776,7 +776,7 @@ GemvFn pick_gemv(int K) {
 int rows_per_wave(int K) { return K >= 2048 ? 1 : 2048 / K; }
 int stage_rows_rt(int K, int MR, bool gateup) {
   const int lpr = K >= 2048 ? 64 : K / 32;
-  const int want = gateup ? 1 : 8;
+  const int want = gateup ? 1 : 4;
   return want < lpr / MR ? want : lpr / MR;
 }
 
