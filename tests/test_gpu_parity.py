@@ -589,3 +589,56 @@ def test_limit_shapes_against_the_oracle(shape):
     if shape == "one_expert":
         assert st["misses"] == 1 and st["hits"] == sum(1 for M in Ms if M <= 16) - 1
     sc.close()
+
+
+def test_graph_replay_of_multi_row_and_staged_prefill_steps():
+    """Captured steps of 4 rows (streaming gate/up, matrix-core down), 8 rows
+    (matrix cores for both) and 24 rows (a prefill chunk staged 3 experts per
+    group: several fill / gate/up / down launches in one step), replayed in
+    turn with new inputs and eager work in between, against the oracle."""
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    Ms = (4, 8, 24)
+    log("graph capture + replay: tiny, M in %s, prefill staged 3 per group" % (Ms,))
+    sc = make_cache(cfg, max_rows=max(Ms), prefill_stage=3)
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(61)
+    E, H = cfg.n_experts, cfg.hidden
+    bufs = {M: (torch.zeros((M, E), dtype=torch.float32, device="cuda"),
+                torch.zeros((M, H), dtype=torch.int16, device="cuda"),
+                torch.zeros((M, H), dtype=torch.float32, device="cuda")) for M in Ms}
+    s = torch.cuda.Stream()
+    graphs = {}
+    torch.cuda.synchronize()
+    for M in Ms:
+        z, x, y = bufs[M]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            g.capture_begin()
+            sc.decode(0, z, x, y, stream=s)
+            g.capture_end()
+        graphs[M] = g
+    torch.cuda.synchronize()
+    stepper = GpuStepper(sc)
+    for t in range(30):
+        M = Ms[t % len(Ms)]
+        z, x, y = bufs[M]
+        zh = rng.standard_normal((M, E)).astype(np.float32)
+        zh[:, :3] += 1.0
+        xh = activations(cfg, 0, 700 + t, M)
+        z.copy_(torch.from_numpy(zh))
+        x.copy_(torch.from_numpy(xh.view(np.int16)))
+        graphs[M].replay()
+        torch.cuda.synchronize()
+        y_o, rec, ids_o, w_o = orc.decode(zh, xh)
+        assert rel_l2(y.cpu().numpy(), y_o) <= Y_TOL, (t, M)
+        if M > 16:
+            assert rec.bypass
+        assert [tuple(e[1:]) for e in stepper.new_events()] == rec.events, (t, M)
+        _check_state(sc, 0, orc.state)
+        _ = (y * 2).sum().item()     # unrelated eager work between replays
+    _check_counters(sc, 0, orc.state)
+    st = sc.stats(0)
+    log("graph multi-row: stats %s" % st)
+    assert st["bypass_steps"] >= 10 and st["misses"] > 0
+    sc.close()
