@@ -802,9 +802,9 @@ int mr_for(int M) { return M == 1 ? 1 : 2; }
 
 // Rows per step from which each product runs on the matrix cores (all-hit GLM
 // layer, drafted rows, µs per kernel, streaming against matrix cores): gate/up
-// 77 / 81 at M = 4, 110 / 84 at 6, 141 / 101 at 8; down 39 / 39 at M = 2,
-// 62 / 41 at 3.  The two-pick streaming down kernel holds about 480 VGPRs (one
-// wavefront per SIMD).
+// 45 / 56 at M = 2, 65 / 58 at 3, 80 / 73 at 4; down 39 / 39 at M = 2, 62 / 41
+// at 3.  The two-pick streaming kernels hold 300-480 VGPRs (one wavefront per
+// SIMD).
 constexpr int kMfmaMinRowsGateup = SC_MFMA_MIN_ROWS_GATEUP;
 constexpr int kMfmaMinRowsDown = SC_MFMA_MIN_ROWS_DOWN;
 

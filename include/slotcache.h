@@ -114,7 +114,7 @@ typedef struct {
  * gate/up (resp. down) product on the matrix cores; their rows need not be
  * bit-equal to the same rows decoded alone (the outputs stay within the same
  * tolerance of the exact result). */
-#define SC_MFMA_MIN_ROWS_GATEUP 5
+#define SC_MFMA_MIN_ROWS_GATEUP 3
 #define SC_MFMA_MIN_ROWS_DOWN 3
 
 typedef struct {
