@@ -135,13 +135,6 @@ __device__ __forceinline__ void fp4x8_f32(uint32_t c, f32x2 (&w)[4]) {
   w[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
 }
 
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 // Sum over one lane's 32 elements of one chunk: codes q (16 B), two block
 // scales in sc (bytes 0, 1), bf16 activation pairs xv[16].
 __device__ __forceinline__ float seg_dot_bf16(const uint4& q, uint32_t sc, const uint32_t* xv) {
@@ -196,23 +189,57 @@ __device__ __forceinline__ float seg_dot_f32(const uint4& q, uint32_t sc, const 
 // butterfly: while more than one value is left, each step trades half of the
 // values with the partner lane, so a lane ends up holding the group sum of one
 // value, index (lane % LPR) / (LPR / NV).
+//
+// The exchanges stay in registers.  Steps 32 and 16 use the gfx950 lane-swap
+// instructions (v_permlane32_swap / v_permlane16_swap: the upper 32 lanes, or
+// the odd 16-lane rows, of one register trade places with the lower lanes, or
+// even rows, of another), so one instruction exchanges a pair of values; steps
+// 8, 4, 2 and 1 read the partner through DPP: row mirror (lane ^ 15), half-row
+// mirror (lane ^ 7) and two quad permutes (lane ^ 2, lane ^ 1).  Every step
+// pairs lanes that differ in bit O, both partners add the same two numbers,
+// and the six pairings span all lane bits: each value is summed over its row
+// group by the same tree whatever NV is, and every lane that holds it holds
+// the same bits.
+template <int O>
+__device__ __forceinline__ float dpp_partner(float v) {
+  constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4E : 0xB1;
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), ctrl, 0xF, 0xF, false));
+}
+
+// a, b -> the step-O pair sums: lanes below bit O hold a's sum, lanes above it b's
+template <int O>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  static_assert(O == 32 || O == 16, "lane swaps exist for 32 and 16");
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 template <int O, int C>
 struct XRed {
   __device__ static __forceinline__ void run(float* v, int lane) {
     if constexpr (O == 0) {
       return;
-    } else if constexpr (C > 1) {
-      const bool up = (lane & O) != 0;
-#pragma unroll
-      for (int i = 0; i < C / 2; ++i) {
-        const float send = up ? v[i] : v[i + C / 2];
-        const float keep = up ? v[i + C / 2] : v[i];
-        v[i] = keep + __shfl_xor(send, O);
-      }
-      XRed<O / 2, C / 2>::run(v, lane);
     } else {
-      v[0] += __shfl_xor(v[0], O);
-      XRed<O / 2, 1>::run(v, lane);
+      if constexpr (O >= 16) {
+#pragma unroll
+        for (int i = 0; i < (C > 1 ? C / 2 : 1); ++i) v[i] = swap_add<O>(v[i], v[C > 1 ? i + C / 2 : 0]);
+      } else if constexpr (C > 1) {
+        const bool up = (lane & O) != 0;
+#pragma unroll
+        for (int i = 0; i < C / 2; ++i) {
+          const float send = up ? v[i] : v[i + C / 2];
+          const float keep = up ? v[i + C / 2] : v[i];
+          v[i] = keep + dpp_partner<O>(send);
+        }
+      } else {
+        v[0] += dpp_partner<O>(v[0]);
+      }
+      XRed<O / 2, (C > 1 ? C / 2 : 1)>::run(v, lane);
     }
   }
 };
