@@ -412,7 +412,7 @@ def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True):
     return bad
 
 
-@pytest.mark.parametrize("shape", ["tiny", "glm32"])
+@pytest.mark.parametrize("shape", ["tiny", "glm32", "h1024_i512"])
 def test_batch_invariant_rows(shape):
     """SC_FLAG_BATCH_INVARIANT: every row of an M-row step (drafted rows sharing
     picks, M up to 16, and a prefill-sized bypass step) is bit-equal to the
@@ -423,6 +423,9 @@ def test_batch_invariant_rows(shape):
     if shape == "glm32":
         g = CONFIGS["glm"]
         cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 32, rows=24, steps=1, seed=g.seed)
+    elif shape == "h1024_i512":
+        # 16- and 32-lane row groups: the two-pick down kernel sums eight values per row group
+        cfg = WorkloadConfig("h1024_i512", 1024, 512, 32, 4, 32, rows=24, steps=1, seed=71)
     log("batch invariance: %s" % shape)
     E = cfg.n_experts
     inv = make_cache(cfg, n_layers=1, slots=[E], max_rows=24, batch_invariant=True)
@@ -588,6 +591,38 @@ def test_limit_shapes_against_the_oracle(shape):
         assert st["bypass_steps"] == len(Ms)
     if shape == "one_expert":
         assert st["misses"] == 1 and st["hits"] == sum(1 for M in Ms if M <= 16) - 1
+    sc.close()
+
+
+# Layer shapes beyond the tiny, Flash and GLM ones: each gives the GEMVs other
+# row-group widths (lanes per row: 8, 16, 32 or 64 for K = 256, 512, 1024,
+# >= 2048), so every step of the cross-lane row sums, the matrix-core kernels
+# at other K and a ragged split of rows over wavefronts are exercised.
+OTHER_SHAPES = {"h512_i256": (512, 256), "h1024_i512": (1024, 512), "h2048_i1024": (2048, 1024),
+                "h8192_i256": (8192, 256)}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape", list(OTHER_SHAPES))
+def test_other_layer_shapes_against_the_oracle(shape):
+    """One-row, two-row (streaming), matrix-core and bypass steps on layer
+    shapes with other H and I: bookkeeping bit for bit, outputs to the
+    tolerance, every step's output checked."""
+    H, I = OTHER_SHAPES[shape]
+    E, k, S = 12, 3, 6
+    Ms = [1, 1, 2, 3, 1, 4, 17, 1, 2, 1, 5, 1]
+    cfg = WorkloadConfig("shape_" + shape, H, I, E, k, S, rows=17, steps=len(Ms), seed=53)
+    log("layer shape %s: H=%d I=%d (E=%d k=%d S=%d, M in %s)" % (shape, H, I, E, k, S, Ms))
+    sc = make_cache(cfg, max_rows=17, gs_mode="uniform", prefill_stage=2)
+    orc = _oracle_layer(cfg, S, "uniform")
+    rng = np.random.default_rng(59)
+    zs = [rng.standard_normal((17, E)).astype(np.float32) for _ in Ms]
+    for z in zs:
+        z[:, :2] += 1.0
+    worst = _run_trace(cfg, sc, orc, len(Ms), lambda t: Ms[t], lambda t: zs[t])
+    st = sc.stats(0)
+    log("shape %s: worst rel L2 %.3g, stats %s" % (shape, worst, st))
+    assert st["misses"] > 0 and st["bypass_steps"] >= 1
     sc.close()
 
 
