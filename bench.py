@@ -50,6 +50,10 @@ def parse():
                          "staged 64 experts at a time and read in place; prints one JSON line")
     ap.add_argument("--dump-steps", default="",
                     help="write the timed steps' all-hit indices and gate/up event durations to this JSON file")
+    ap.add_argument("--pmc-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/pmc_gateup_glm_m1.json and pmc_down_glm_m1.json from the rocprofv3 "
+                         "--pmc counter files of a bench run and of the --calibrate-copy run")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "STEPS_JSON"),
                     help="only summarize a rocprofv3 kernel trace of this bench: gate/up durations over the "
                          "all-hit timed launches listed by --dump-steps")
@@ -190,6 +194,79 @@ def sweep_rows(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_s
     sc.close()
 
 
+def gemv_bytes(cfg):
+    """Algorithmic bytes of the one-row gate/up and down launches: the U = k
+    experts' weight codes and scales, the activation row, h written (gate/up)
+    and read (down), the per-pick down outputs."""
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    U = k  # M=1: the k picks are distinct experts
+    gateup = U * (2 * I * H // 2 + 2 * I * H // 16) + H * 2 + k * I * 4
+    down = U * (H * I // 2 + H * I // 16) + k * I * 4 + k * H * 4
+    return gateup, down
+
+
+PMC_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch "
+    "-o run -- python3 -u $REPO/bench.py --steps 20 --warmup 4 --no-cpu-baseline",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write "
+    "-o run -- python3 -u $REPO/bench.py --steps 20 --warmup 4 --no-cpu-baseline",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch_copy "
+    "-o run -- python3 -u $REPO/bench.py --calibrate-copy",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write_copy "
+    "-o run -- python3 -u $REPO/bench.py --calibrate-copy",
+    "cd $REPO && python3 bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
+    "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_fetch_copy/run_counter_collection.csv "
+    "gpurun_out/pmc_write_copy/run_counter_collection.csv",
+]
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of the one-row GEMVs from rocprofv3 counters.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, summed over the counter's
+    instances) come from separate runs; each is scaled by what the same
+    counter reads for a plain 1 GiB device copy (--calibrate-copy), and the
+    median over a kernel's dispatches is kept.  The result carries the sha256
+    of the kernel source so that the bench reports it only for that source."""
+    import csv
+    import statistics
+
+    def per_dispatch(path, counter, name_part):
+        by, full = {}, None
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                by[r["Dispatch_Id"]] = by.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                full = full or r["Kernel_Name"]
+        return list(by.values()), full
+
+    gib = 1 << 30
+    cf = max(per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")[0])
+    cw = max(per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")[0])
+    ff, wf = cf * 1024 / gib, cw * 1024 / gib
+    from synth import CONFIGS
+    gb, db = gemv_bytes(CONFIGS["glm"])
+    src = source_hash()
+    for key, name, algo in (("gateup_glm_m1", KERNEL_NAMES["gateup"], gb), ("down_glm_m1", KERNEL_NAMES["down"], db)):
+        f, full = per_dispatch(fetch_csv, "FETCH_SIZE", name)
+        w, _ = per_dispatch(write_csv, "WRITE_SIZE", name)
+        if not f or not w:
+            raise SystemExit("no %s dispatches of %s in the counter files" % ("FETCH_SIZE" if not f else "WRITE_SIZE", name))
+        fm, wm = statistics.median(f), statistics.median(w)
+        bpl = int(round(fm * 1024 / ff + wm * 1024 / wf))
+        out = {"kernel": (full.split(">(")[0] + ">") if ">(" in full else full,
+               "workload": "GLM-shaped MoE layer, H6144 I2048, 256 experts, top-8, 128 slots, M=1 "
+                           "(bench.py --steps 20 --warmup 4)",
+               "source_sha256": src, "fetch_size_kib_median": fm, "write_size_kib_median": wm, "dispatches": len(f),
+               "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 1 GiB)", "bytes_read": gib,
+                               "bytes_written": gib, "fetch_size_kib": cf, "write_size_kib": cw,
+                               "fetch_factor": ff, "write_factor": wf},
+               "bytes_per_launch": bpl, "algorithmic_bytes_per_launch": algo,
+               "traffic_over_algorithmic": bpl / algo, "commands": PMC_COMMANDS}
+        with open(os.path.join(ROOT, "profiles", "pmc_%s.json" % key), "w") as fh:
+            json.dump(out, fh, indent=1)
+        print(key, out["kernel"], "bytes/launch", bpl, "ratio", round(bpl / algo, 4), "dispatches", len(f))
+
+
 def trace_summary(trace_csv, steps_json):
     """Average rocprofv3 duration of the gate/up kernel over the all-hit timed launches.
 
@@ -326,6 +403,9 @@ def main():
     if a.trace_summary:
         trace_summary(*a.trace_summary)
         return
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X "
               "(no collectives); --gpus %d is not supported" % a.gpus, file=sys.stderr)
@@ -452,9 +532,7 @@ def main():
 
     B = sc.blob_bytes
     H, I, k = cfg.hidden, cfg.inter, cfg.top_k
-    U = k  # M=1: the k picks are distinct experts
-    gateup_bytes = U * (2 * I * H // 2 + 2 * I * H // 16) + H * 2 + k * I * 4
-    down_bytes = U * (H * I // 2 + H * I // 16) + k * I * 4 + k * H * 4
+    gateup_bytes, down_bytes = gemv_bytes(cfg)
     # roofline: the gate/up kernel on the timed steps without a miss (a miss step's slot was just
     # written by the fill, so part of it can come from the Infinity Cache)
     gu = float(np.mean(gu_us[hit_idx])) if hit_idx else float("nan")
