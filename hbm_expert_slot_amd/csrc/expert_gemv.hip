@@ -653,17 +653,17 @@ struct GemvMfmaL {
             const int r0 = (tile0 + rt) * 16 + 4 * g;      // r0 % 8 is 0 or 4
             float* row = a.out + (size_t)p * a.rows;
             if (GATEUP && a.split_h) {
-              bf16x4 hi, lo;
+              bf16x4 hi4, lo4;
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 __bf16 h, l;
                 split_bf16(v[j], h, l);
-                hi[j] = h;
-                lo[j] = l;
+                hi4[j] = h;
+                lo4[j] = l;
               }
               __bf16* grp = reinterpret_cast<__bf16*>(row) + (r0 / 8) * 16 + (r0 % 8);
-              *reinterpret_cast<bf16x4*>(grp) = hi;
-              *reinterpret_cast<bf16x4*>(grp + 8) = lo;
+              *reinterpret_cast<bf16x4*>(grp) = hi4;
+              *reinterpret_cast<bf16x4*>(grp + 8) = lo4;
             } else {
               *reinterpret_cast<float4*>(row + r0) = make_float4(v[0], v[1], v[2], v[3]);
             }
@@ -815,7 +815,7 @@ int gemv_blocks(long stages, int cap) {
   return (int)blocks;
 }
 
-// The gate/up kernels hold about 165 VGPRs, three wavefronts per SIMD: 768
+// The gate/up kernels hold about 152 VGPRs, three wavefronts per SIMD: 768
 // blocks of four wavefronts are all resident at once.  With 1024 the last 256
 // blocks only started once the first ones had finished (about 12 us in) and
 // streamed alone at the end (GLM layer, M=1: 21.2 against 20.6 us).
