@@ -626,6 +626,45 @@ def test_other_layer_shapes_against_the_oracle(shape):
     sc.close()
 
 
+def _random_layer(rng, i):
+    """A small random layer: expert count, top-k, slots, pins, row mix, staging."""
+    H, I = [(256, 128), (512, 256), (256, 256), (1024, 128)][i % 4]
+    E = int(rng.integers(1, 41))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    S = int(rng.integers(1, E + 1))
+    npin = int(rng.integers(0, S + 1)) if rng.random() < 0.3 else 0
+    max_rows = int(rng.choice([1, 4, 17, 24]))
+    Ms = [int(rng.integers(1, max_rows + 1)) for _ in range(14)]
+    stage = int(rng.integers(1, 6)) if rng.random() < 0.5 else 0
+    return H, I, E, k, S, npin, max_rows, Ms, stage
+
+
+@pytest.mark.timeout(600)
+def test_random_layers_against_the_oracle():
+    """Twelve seeded random layers (1-40 experts, top-1..8, 1..E slots, pins on
+    some, row mixes up to 24 with and without prefill staging, four H x I
+    shapes): every step's bookkeeping bit for bit and output to the tolerance."""
+    torch_cuda()
+    rng = np.random.default_rng(2024)
+    for i in range(12):
+        H, I, E, k, S, npin, max_rows, Ms, stage = _random_layer(rng, i)
+        log("random layer %d: H=%d I=%d E=%d k=%d S=%d pins=%d max_rows=%d stage=%d M=%s"
+            % (i, H, I, E, k, S, npin, max_rows, stage, Ms))
+        cfg = WorkloadConfig("rand%d" % i, H, I, E, k, S, rows=max_rows, steps=len(Ms), seed=300 + i)
+        sc = make_cache(cfg, max_rows=max_rows, gs_mode="uniform", prefill_stage=stage)
+        orc = _oracle_layer(cfg, S, "uniform")
+        if npin:
+            pins = [int(e) for e in rng.permutation(E)[:npin]]
+            sc.pin(0, pins)
+            orc.state.pin(pins)
+        zs = [rng.standard_normal((max_rows, E)).astype(np.float32) for _ in Ms]
+        for z in zs:
+            z[:, : max(1, E // 6)] += 1.0
+        worst = _run_trace(cfg, sc, orc, len(Ms), lambda t: Ms[t], lambda t: zs[t])
+        log("random layer %d: worst rel L2 %.3g, stats %s" % (i, worst, sc.stats(0)))
+        sc.close()
+
+
 def test_graph_replay_of_multi_row_and_staged_prefill_steps():
     """Captured steps of 4 rows (streaming gate/up, matrix-core down), 8 rows
     (matrix cores for both) and 24 rows (a prefill chunk staged 3 experts per
