@@ -67,6 +67,7 @@ def _run_trace(cfg, sc, orc, steps, rows_fn, logits_fn, y_steps=None, state_ever
         x = activations(cfg, 0, t, M)
         want_y = y_steps is None or t in y_steps
         y, ids, w, byp = g.step(z, x)
+        assert np.isfinite(y).all(), t          # every step, also those whose output is not compared
         ev = g.new_events()
         o = orc.decode(z, x, with_output=want_y)
         r = _check_step(t, (y, ids, w, byp, ev), o, None, want_y)
