@@ -113,7 +113,8 @@ __device__ __forceinline__ uint4 ld16_stream(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load((g_u32x4*)(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *(g_u16*)(p); }
+// The block scales are streamed once per step as well.
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return __builtin_nontemporal_load((g_u16*)(p)); }
 
 // Wavefront index as a uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
