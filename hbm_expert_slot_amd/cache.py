@@ -14,10 +14,14 @@ class SlotCache:
     """prefill_stage: experts a prefill chunk (more than 16 rows) stages into
     HBM per group before computing them (0: read them in place from the
     pinned host store).  64 is the group size of the pages' prefill-groups
-    knob; the staging area costs prefill_stage * blob_bytes of workspace."""
+    knob; the staging area costs prefill_stage * blob_bytes of workspace.
+
+    overlap_fill: on one-row steps, compute the resident experts' gate/up
+    while the misses are copied (SC_FLAG_OVERLAP_FILL); same output bits."""
 
     def __init__(self, n_layers, hidden, inter, n_experts, top_k, slots, max_rows,
-                 n_banks=1, event_capacity=0, device="cuda", batch_invariant=False, prefill_stage=64):
+                 n_banks=1, event_capacity=0, device="cuda", batch_invariant=False, prefill_stage=64,
+                 overlap_fill=False):
         import torch
 
         self.torch = torch
@@ -28,7 +32,8 @@ class SlotCache:
         self.n_experts, self.top_k, self.max_rows, self.n_banks = n_experts, top_k, max_rows, n_banks
         self.cfg = B.make_config(n_layers, hidden, inter, n_experts, top_k, self.slots, max_rows,
                                  n_banks, event_capacity,
-                                 flags=B.SC_FLAG_BATCH_INVARIANT if batch_invariant else 0,
+                                 flags=((B.SC_FLAG_BATCH_INVARIANT if batch_invariant else 0)
+                                        | (B.SC_FLAG_OVERLAP_FILL if overlap_fill else 0)),
                                  prefill_stage=prefill_stage)
         self.sizes = B.slotcache_query_sizes(self.cfg)
         self.blob_bytes = self.sizes.blob_bytes

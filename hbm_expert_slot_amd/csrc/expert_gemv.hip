@@ -257,7 +257,11 @@ struct XRed {
 // kernel takes U from the launch instead of the header and skips the CSR
 // lookups, so a wavefront's first weight loads wait for one pointer load only
 // and its activation loads for none.
-template <int K, int MR, int R, bool GATEUP, bool SINGLE = false>
+//
+// PART (one-row gate/up only) splits a step around its fill: 1 = the experts
+// the fill does not write (the copy runs beside them), 2 = the ones it writes,
+// taken from the remap's resident-first order once the copy is done.
+template <int K, int MR, int R, bool GATEUP, bool SINGLE = false, int PART = 0>
 struct Gemv {
   using G = Geo<K>;
   static constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
@@ -340,15 +344,25 @@ struct Gemv {
     }
   }
 
-  __device__ static __forceinline__ void run(const GemvArgs& a) {
+  // vblock / vgrid: this block and the launch's block count, or those of the
+  // launch's product blocks when it shares them with a copy.
+  __device__ static __forceinline__ void run(const GemvArgs& a, int vblock, int vgrid) {
     static_assert(!SINGLE || MR == 1, "one-row steps have one pick per expert");
+    static_assert(PART == 0 || (SINGLE && GATEUP), "only one-row gate/up steps are split");
     int lo = 0, U = a.k;
     if (!SINGLE) launch_uniques(a, a.hdr[H_UNIQUE], lo, U);
+    // filled experts: the last nf of the resident-first order
+    int nf = PART != 0 ? a.hdr[H_MISS] : 0;
+    nf = nf < 0 ? 0 : nf > a.k ? a.k : nf;
+    if (PART == 2) {
+      lo = a.k - nf;
+      U = nf;
+    }
     if (U <= 0) return;
     const int lane = threadIdx.x & 63;
     const int seg = lane % LPR, rsub = lane / LPR;
-    const int nwaves = gridDim.x * (kGemvThreads / 64);
-    const int gw = blockIdx.x * (kGemvThreads / 64) + wave_id();
+    const int nwaves = vgrid * (kGemvThreads / 64);
+    const int gw = vblock * (kGemvThreads / 64) + wave_id();
     const int spu = a.rows / RPW;
     int wpu = nwaves / U;
     if (wpu < 1) wpu = 1;
@@ -358,13 +372,20 @@ struct Gemv {
     const int ntask = U * wpu;
     for (int task = gw; task < ntask; task += nwaves) {
       const int j = task / wpu, sub = task - (task / wpu) * wpu;
-      const int u = SINGLE ? j : unique_at(a, lo, j);
+      const int u = PART == 2 ? a.order[lo + j] : SINGLE ? j : unique_at(a, lo, j);
       // a task owns row steps base + i * stride, i < n
       const int base = sub * q + (sub < rem ? sub : rem), stride = 1;
       const int n = q + (sub < rem ? 1 : 0);
       if (n <= 0) continue;
       const uint8_t* blob = a.uniq_ptr[u];
       const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
+      if (PART == 1 && nf > 0) {
+        // part 1 keeps every expert's share of the waves, so an all-hit step
+        // (nf = 0) runs as the plain kernel does; a filled expert's waves sit out
+        bool filled = false;
+        for (int i = a.k - nf; i < a.k; ++i) filled |= a.order[i] == u;
+        if (filled) continue;
+      }
       const int off0 = SINGLE ? u : a.uniq_off[u], off1 = SINGLE ? u + 1 : a.uniq_off[u + 1];
       const uint8_t* code_base = blob + a.code_off + seg * 16;
       const uint8_t* scale_base = blob + a.scale_off + seg * 2;
@@ -416,7 +437,7 @@ struct Gemv {
 template <int K, int MR, int R, bool GATEUP, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   span_start(a.span);
-  Gemv<K, MR, R, GATEUP, SINGLE>::run(a);
+  Gemv<K, MR, R, GATEUP, SINGLE>::run(a, blockIdx.x, gridDim.x);
   span_end(a.span);
 }
 
@@ -707,9 +728,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma_lds(GemvArgs a) {
 // keeps four loads in flight across blob boundaries; with nothing to copy it
 // exits.  Entries whose destination is null (a miss the remap could not
 // place) are skipped.
-__global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t* const* src,
-                                               uint8_t* const* dst, long n16, int group, int G, uint64_t* span) {
-  span_start(span);
+// The copy runs over `vgrid` blocks of 256 threads, of which this is `vblock`.
+__device__ __forceinline__ void fill_body(const int32_t* hdr, const uint8_t* const* src, uint8_t* const* dst,
+                                          long n16, int group, int G, int vblock, int vgrid) {
   int first = 0, count = hdr[H_MISS];
   if (group >= 0) {
     const int ns = hdr[H_STAGED];
@@ -720,8 +741,8 @@ __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t*
   src += first;
   dst += first;
   const long total = (long)count * n16;
-  const long stride = (long)gridDim.x * blockDim.x;
-  long o = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long stride = (long)vgrid * blockDim.x;
+  long o = (long)vblock * blockDim.x + threadIdx.x;
   for (; o + 3 * stride < total; o += 4 * stride) {
     uint4 v[4];
 #pragma unroll
@@ -739,7 +760,48 @@ __global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t*
     const long i = o / n16;
     if (dst[i]) *reinterpret_cast<uint4*>(dst[i] + (o - i * n16) * 16) = ld16(src[i] + (o - i * n16) * 16);
   }
+}
+
+__global__ __launch_bounds__(256) void k_fill(const int32_t* hdr, const uint8_t* const* src,
+                                               uint8_t* const* dst, long n16, int group, int G, uint64_t* span) {
+  span_start(span);
+  fill_body(hdr, src, dst, n16, group, G, blockIdx.x, gridDim.x);
   span_end(span);
+}
+
+// Overlapped fill of a one-row step.  The copy is bound by the host link, and
+// a concurrent HBM stream does not slow it, so the experts it does not write
+// are computed while it runs: blocks [0, nb_fill) copy the misses into their
+// slots (first, so that they start at once), the others compute gate/up for
+// the resident experts.  The copied experts' gate/up follows in
+// k_gemv_filled.  The pages name asynchronous miss fills as what could cut
+// the copy's cost ("GB300 GLM 5.3 Testing", September 13 update of
+// "Speculation: what is holding the GB300 back, and what probably wins next").
+struct FillArgs {
+  const int32_t* hdr;
+  const uint8_t* const* src;
+  uint8_t* const* dst;
+  long n16;
+  uint64_t* span;
+};
+
+template <int K>
+__global__ __launch_bounds__(kGemvThreads) void k_fill_gateup(FillArgs f, GemvArgs a, int nb_fill) {
+  const int b = blockIdx.x;
+  if (b < nb_fill) {
+    span_start(f.span, b);
+    fill_body(f.hdr, f.src, f.dst, f.n16, -1, 0, b, nb_fill);
+    span_end(f.span, b);
+  } else {
+    span_start(a.span, b - nb_fill);
+    Gemv<K, 1, 1, true, true, 1>::run(a, b - nb_fill, gridDim.x - nb_fill);
+    span_end(a.span, b - nb_fill);
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_filled(GemvArgs a) {
+  Gemv<K, 1, 1, true, true, 2>::run(a, blockIdx.x, gridDim.x);
 }
 
 // y[m][r] = sum over j = 0..k-1 of w[m][j] * part[m*k + j][r], in rank order.
@@ -890,8 +952,7 @@ static GemvArgs base_args(const Workspace& W, const float* gs, int group) {
   return a;
 }
 
-hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
-                         bool mfma, int group, hipStream_t st, KEvents ev) {
+static GemvArgs gateup_args(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int group) {
   GemvArgs a = base_args(W, gs, group);
   a.operand = x;
   a.out = W.h;
@@ -900,6 +961,12 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.up_row0 = sh.I;
   a.code_off = 0;
   a.scale_off = sh.off_w13s;
+  return a;
+}
+
+hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
+                         bool mfma, int group, hipStream_t st, KEvents ev) {
+  GemvArgs a = gateup_args(sh, W, gs, x, group);
   a.split_h = mfma && M >= kMfmaMinRowsDown;   // the down product of this step runs on the matrix cores
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (mfma && M >= kMfmaMinRowsGateup) {
@@ -916,6 +983,64 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   const int blocks = gemv_blocks(stages, kGateupBlocks);
   a.span = ev.span_for(blocks);
   return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
+}
+
+typedef void (*FillGateupFn)(FillArgs, GemvArgs, int);
+
+static FillGateupFn pick_fill_gateup(int K) {
+  switch (K) {
+    case 256: return k_fill_gateup<256>;
+    case 512: return k_fill_gateup<512>;
+    case 1024: return k_fill_gateup<1024>;
+    case 2048: return k_fill_gateup<2048>;
+    case 4096: return k_fill_gateup<4096>;
+    case 6144: return k_fill_gateup<6144>;
+    case 8192: return k_fill_gateup<8192>;
+    default: return nullptr;
+  }
+}
+
+static GemvFn pick_gemv_filled(int K) {
+  switch (K) {
+    case 256: return k_gemv_filled<256>;
+    case 512: return k_gemv_filled<512>;
+    case 1024: return k_gemv_filled<1024>;
+    case 2048: return k_gemv_filled<2048>;
+    case 4096: return k_gemv_filled<4096>;
+    case 6144: return k_gemv_filled<6144>;
+    case 8192: return k_gemv_filled<8192>;
+    default: return nullptr;
+  }
+}
+
+// Product blocks of a one-row gate/up launch (as launch_gateup picks them).
+static int one_row_gateup_blocks(const Shape& sh) {
+  const long maxu = sh.k < sh.E ? sh.k : sh.E;
+  return gemv_blocks(maxu * (sh.I / rows_per_wave(sh.H)) / stage_rows_rt(sh.H, 1, true), kGateupBlocks);
+}
+
+hipError_t launch_fill_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x,
+                              hipStream_t st, KEvents ev_fill, KEvents ev) {
+  FillGateupFn fn = pick_fill_gateup(sh.H);
+  if (!fn) return hipErrorInvalidValue;
+  GemvArgs a = gateup_args(sh, W, gs, x, -1);
+  const int blocks = one_row_gateup_blocks(sh);
+  a.span = ev.span_for(blocks);
+  FillArgs f;
+  f.hdr = W.hdr;
+  f.src = W.miss_src;
+  f.dst = W.miss_dst;
+  f.n16 = (long)(sh.blob / 16);
+  f.span = ev_fill.span_for(kFillBlocks);
+  return sc_launch(fn, dim3(kFillBlocks + blocks), dim3(kGemvThreads), st, ev, f, a, kFillBlocks);
+}
+
+hipError_t launch_gateup_filled(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x,
+                                hipStream_t st) {
+  GemvFn fn = pick_gemv_filled(sh.H);
+  if (!fn) return hipErrorInvalidValue;
+  return sc_launch(fn, dim3(one_row_gateup_blocks(sh)), dim3(kGemvThreads), st, KEvents(),
+                   gateup_args(sh, W, gs, x, -1));
 }
 
 hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, int group,

@@ -61,7 +61,9 @@ struct Workspace {
   uint8_t** miss_dst;           // [Pmax]
   float* h;                     // [Pmax][I]  SiLU(gate) * up, per pick
   float* part;                  // [Pmax][H]  down projection, per pick
-  int32_t* uniq_order;          // [Pmax]  staged prefill: resident uniques, then staged ones in staging order
+  int32_t* uniq_order;          // [Pmax]  the uniques found resident, then the others: misses in miss order
+                                //         (cached step), staged ones in staging order (staged prefill);
+                                //         unique order on other bypass steps
   uint8_t* stage;               // [stage_n] blobs: prefill staging area (null when stage_n == 0)
   int32_t stage_n;              // G, experts per prefill group (0: no staging)
 };
@@ -123,16 +125,20 @@ struct KEvents {
 // span[b * kSpanSlots + 1 + w].  Kernels of a timed step write them; the host
 // keeps the stamps not older than the step's routing kernel start.
 constexpr int kSpanSlots = 5;   // start + one end per wavefront (at most 4 per block)
-__device__ __forceinline__ void span_start(uint64_t* span) {
-  if (span && threadIdx.x == 0) span[(size_t)blockIdx.x * kSpanSlots] = (uint64_t)wall_clock64();
+// b: the block's index in the launch, or in its part of a launch whose blocks
+// do two jobs (the stamps of each job go to a region of their own).
+__device__ __forceinline__ void span_start(uint64_t* span, unsigned b) {
+  if (span && threadIdx.x == 0) span[(size_t)b * kSpanSlots] = (uint64_t)wall_clock64();
 }
-__device__ __forceinline__ void span_end(uint64_t* span) {
+__device__ __forceinline__ void span_end(uint64_t* span, unsigned b) {
   if (span) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wavefront's stores are done
     if ((threadIdx.x & 63) == 0)
-      span[(size_t)blockIdx.x * kSpanSlots + 1 + (threadIdx.x >> 6)] = (uint64_t)wall_clock64();
+      span[(size_t)b * kSpanSlots + 1 + (threadIdx.x >> 6)] = (uint64_t)wall_clock64();
   }
 }
+__device__ __forceinline__ void span_start(uint64_t* span) { span_start(span, blockIdx.x); }
+__device__ __forceinline__ void span_end(uint64_t* span) { span_end(span, blockIdx.x); }
 
 template <typename F, typename... Args>
 inline hipError_t sc_launch(F kernel, dim3 grid, dim3 block, hipStream_t st, KEvents ev, Args... args) {
@@ -155,6 +161,17 @@ hipError_t launch_fill(const Shape& sh, const Workspace& W, int group, hipStream
 // mfma: the matrix-core kernels may serve M >= 12 (off: the streaming kernels for every M).
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
                          bool mfma, int group, hipStream_t st, KEvents ev);
+// Overlapped fill of a one-row step (SC_FLAG_OVERLAP_FILL), two launches in
+// place of launch_fill + launch_gateup.  The first shares its blocks between
+// the copy of the step's misses (stamps in ev_fill's region) and the gate/up
+// products of the experts the copy does not write (stamps in ev's region, and
+// ev's events bracket the launch); the second computes the copied experts'
+// gate/up once the copy is done (no stamps).  Both read the step's expert
+// order from the remap: experts it found resident first, then the misses.
+hipError_t launch_fill_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x,
+                              hipStream_t st, KEvents ev_fill, KEvents ev);
+hipError_t launch_gateup_filled(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x,
+                                hipStream_t st);
 hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int M, bool mfma, int group,
                        hipStream_t st, KEvents ev);
 hipError_t launch_combine(const Shape& sh, const Workspace& W, float* y, int M, hipStream_t st,

@@ -489,9 +489,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       }
       __syncthreads();
     }
-    // ---- stamp the clock, publish slot pointers ----------------------------
+    // ---- stamp the clock, publish slot pointers and the resident-first order
+    const int nres = U - nmiss;
     for (int u = tid; u < U; u += kRouteThreads) {
-      const int sl = s_uslot[u];
+      const int sl = s_uslot[u], i = s_umiss[u];
+      a.W.uniq_order[i >= 0 ? nres + i : -1 - i] = u;
       if (sl < 0) {
         a.W.uniq_ptr[u] = a.L.backing + (size_t)s_uexp[u] * B;
         continue;
@@ -522,6 +524,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     for (int u = tid; u < U; u += kRouteThreads) {
       const int sl = s_uslot[u];
       a.W.uniq_ptr[u] = sl >= 0 ? a.L.slots + (size_t)sl * B : a.L.backing + (size_t)s_uexp[u] * B;
+      a.W.uniq_order[u] = u;
     }
   }
   for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_expert[u] = s_uexp[u];

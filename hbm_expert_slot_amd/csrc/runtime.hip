@@ -118,7 +118,8 @@ sc_status check_config(const sc_config* c) {
     return fail(SC_E_ARG, "max_rows * top_k must be <= %d", kMaxPicks);
   if (c->n_banks < 1 || c->n_banks > c->n_layers) return fail(SC_E_ARG, "n_banks must be in [1, n_layers]");
   if (c->event_capacity < 0) return fail(SC_E_ARG, "event_capacity must be >= 0");
-  if (c->flags & ~(uint32_t)SC_FLAG_BATCH_INVARIANT) return fail(SC_E_ARG, "unknown flags 0x%x", c->flags);
+  if (c->flags & ~(uint32_t)(SC_FLAG_BATCH_INVARIANT | SC_FLAG_OVERLAP_FILL))
+    return fail(SC_E_ARG, "unknown flags 0x%x", c->flags);
   if (c->prefill_stage < 0 || c->prefill_stage > kMaxExperts)
     return fail(SC_E_ARG, "prefill_stage must be in [0, %d]", kMaxExperts);
   if (!c->slots_per_layer) return fail(SC_E_ARG, "slots_per_layer is NULL");
@@ -453,7 +454,16 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
   };
   const bool mfma = !(h->cfg.flags & SC_FLAG_BATCH_INVARIANT);
   e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
-  if (!staged_step(h->W, M)) {
+  if (M == 1 && (h->cfg.flags & SC_FLAG_OVERLAP_FILL)) {
+    // the copy shares a launch with the resident experts' gate/up; the copied
+    // experts' gate/up runs after it
+    KEvents fev = kev(1);
+    if (e == hipSuccess && fev.start) e = hipEventRecord(fev.start, s);
+    if (e == hipSuccess) e = launch_fill_gateup(h->sh, h->W, L.gs, d_x, s, fev, kev(2));
+    if (e == hipSuccess && fev.stop) e = hipEventRecord(fev.stop, s);
+    if (e == hipSuccess) e = launch_gateup_filled(h->sh, h->W, L.gs, d_x, s);
+    if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, -1, s, kev(3));
+  } else if (!staged_step(h->W, M)) {
     if (e == hipSuccess) e = launch_fill(h->sh, h->W, -1, s, kev(1));
     if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, -1, s, kev(2));
     if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, -1, s, kev(3));

@@ -83,7 +83,7 @@ typedef struct {
   int32_t max_rows;               /* largest M the caller will pass, 1..256 */
   int32_t n_banks;                /* host backing banks, 1..n_layers; layer l reads bank l % n_banks */
   int32_t event_capacity;         /* per-layer miss-event ring, records (0 = 4096) */
-  uint32_t flags;                 /* 0 or SC_FLAG_BATCH_INVARIANT */
+  uint32_t flags;                 /* 0, or SC_FLAG_BATCH_INVARIANT and/or SC_FLAG_OVERLAP_FILL */
   int32_t prefill_stage;          /* G, experts staged per prefill group, 0..1024 (see below) */
 } sc_config;
 
@@ -109,6 +109,23 @@ typedef struct {
  * GLM-5.3 explained").  Costs speed from M = 3 on (the matrix-core ranges
  * below). */
 #define SC_FLAG_BATCH_INVARIANT 1u
+
+/* Overlapped miss fill for one-row steps (M = 1).  The copy of the step's
+ * misses into their slots shares one launch with the gate/up products of the
+ * experts it does not write, which run while the copy crosses the host link;
+ * the copied experts' gate/up follows, then down and the combine.  The pages
+ * name asynchronous miss fills as what could take the copy off the critical
+ * path (page "GB300 GLM 5.3 Testing", September 13 update of the section
+ * "Speculation: what is holding the GB300 back, and what probably wins
+ * next").  Outputs, slots and bookkeeping are the same bits as without the
+ * flag.  The trade-off: a step with misses finishes sooner by about the
+ * resident experts' gate/up time, but the copy blocks take wave slots from
+ * the products, so an all-hit step's gate/up runs slower.  Steps of more than
+ * one row are not affected.  With events (moe_layer_decode_ev) the fill
+ * events bracket the shared launch and its spans are its copy blocks'; the
+ * gate/up events and spans are those of its product blocks; the copied
+ * experts' gate/up launch is not timed. */
+#define SC_FLAG_OVERLAP_FILL 2u
 
 /* Without SC_FLAG_BATCH_INVARIANT, steps of at least this many rows run the
  * gate/up (resp. down) product on the matrix cores; their rows need not be

@@ -22,13 +22,13 @@ def torch_cuda():
 
 
 def make_cache(cfg, n_layers=1, slots=None, max_rows=None, n_banks=1, gs_mode="unit",
-               event_capacity=0, n_experts=None, batch_invariant=False, prefill_stage=64):
+               event_capacity=0, n_experts=None, batch_invariant=False, prefill_stage=64, overlap_fill=False):
     from hbm_expert_slot_amd.cache import SlotCache
     E = n_experts or cfg.n_experts
     sc = SlotCache(n_layers, cfg.hidden, cfg.inter, E, cfg.top_k,
                    slots if slots is not None else cfg.slots,
                    max_rows or cfg.rows, n_banks, event_capacity, batch_invariant=batch_invariant,
-                   prefill_stage=prefill_stage)
+                   prefill_stage=prefill_stage, overlap_fill=overlap_fill)
     for b in range(n_banks):
         expert_blobs(cfg, b, range(E), out=sc.backing(b))
         gs = global_scales(cfg, b, gs_mode)[:E]

@@ -71,7 +71,7 @@ def test_prefill_staging_area_is_part_of_the_workspace():
     (dict(hidden=6000), B.SC_E_ARG),
     (dict(hidden=3072), B.SC_E_UNSUPPORTED),
     (dict(inter=64), B.SC_E_UNSUPPORTED),
-    (dict(flags=2), B.SC_E_ARG),
+    (dict(flags=4), B.SC_E_ARG),
     (dict(prefill_stage=-1), B.SC_E_ARG),
     (dict(prefill_stage=1025), B.SC_E_ARG),
 ])

@@ -356,10 +356,9 @@ def _check_slots_hold_their_experts(sc, layer=0):
 
 @pytest.mark.parametrize("shape", ["tiny", "glm48"])
 def test_misses_fill_their_slots_exactly(shape):
-    """Misses are filled by the gate/up launch (read-through of the gate/up rows,
-    copy blocks for the down rows): after a churning mix of one-row, multi-row
-    (experts with several picks) and matrix-core steps every occupied slot must
-    equal its expert's blob."""
+    """After a churning mix of one-row, multi-row (experts with several picks)
+    and matrix-core steps, every occupied slot equals its expert's blob byte
+    for byte: the fill copied each miss whole into its victim slot."""
     cfg = CONFIGS["tiny"]
     if shape == "glm48":
         g = CONFIGS["glm"]
