@@ -180,3 +180,48 @@ def test_overlap_fill_graph_replay_under_churn():
     _check_counters(sc, 0, orc.state)
     assert sc.stats(0)["misses"] > 0
     sc.close()
+
+
+@pytest.mark.timeout(600)
+def test_overlap_fill_random_layers():
+    """Twelve seeded random layers (1-40 experts, top-1..8, 1..E slots, pins
+    on some, prefill staging on some), mostly one-row steps, with the flag:
+    every step's bookkeeping against the oracle and outputs bitwise against
+    the same layer without the flag."""
+    torch_cuda()
+    from test_gpu_parity import _random_layer
+    rng = np.random.default_rng(4048)
+    for i in range(12):
+        H, I, E, k, S, npin, max_rows, Ms, stage = _random_layer(rng, i)
+        Ms = [1 if rng.random() < 0.7 else m for m in Ms]
+        log("overlapped fill, random layer %d: H=%d I=%d E=%d k=%d S=%d pins=%d max_rows=%d stage=%d M=%s"
+            % (i, H, I, E, k, S, npin, max_rows, stage, Ms))
+        cfg = WorkloadConfig("ovrand%d" % i, H, I, E, k, S, rows=max_rows, steps=len(Ms), seed=500 + i)
+        ov = make_cache(cfg, max_rows=max_rows, gs_mode="uniform", prefill_stage=stage, overlap_fill=True)
+        pl = make_cache(cfg, max_rows=max_rows, gs_mode="uniform", prefill_stage=stage)
+        orc = _oracle_layer(cfg, S, "uniform")
+        if npin:
+            pins = [int(e) for e in rng.permutation(E)[:npin]]
+            ov.pin(0, pins)
+            pl.pin(0, pins)
+            orc.state.pin(pins)
+        zs = [rng.standard_normal((max_rows, E)).astype(np.float32) for _ in Ms]
+        for z in zs:
+            z[:, : max(1, E // 6)] += 1.0
+        go, gp = GpuStepper(ov), GpuStepper(pl)
+        worst = 0.0
+        for t, M in enumerate(Ms):
+            z = zs[t][:M]
+            x = activations(cfg, 0, t, M)
+            y, ids, w, byp = go.step(z, x)
+            yp, _, _, _ = gp.step(z, x)
+            assert np.array_equal(y, yp), (i, t, M)
+            ev = go.new_events()
+            gp.new_events()
+            r = _check_step(t, (y, ids, w, byp, ev), orc.decode(z, x), None)
+            worst = max(worst, r)
+            _check_state(ov, 0, orc.state)
+        _check_counters(ov, 0, orc.state)
+        log("overlapped fill, random layer %d: worst rel L2 %.3g, stats %s" % (i, worst, ov.stats(0)))
+        ov.close()
+        pl.close()
