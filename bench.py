@@ -51,7 +51,8 @@ def parse():
                          "staged 64 experts at a time and read in place; prints one JSON line")
     ap.add_argument("--overlap-fill", action="store_true",
                     help="one-row steps copy their misses while the resident experts' gate/up runs in the same "
-                         "launch (SC_FLAG_OVERLAP_FILL); the roofline is then that shared launch's product blocks")
+                         "launch (SC_FLAG_OVERLAP_FILL); the roofline is then that shared launch's product blocks. "
+                         "Applies to the default M=1 workload (the flag changes nothing for steps of several rows)")
     ap.add_argument("--dump-steps", default="",
                     help="write the timed steps' all-hit indices and gate/up event durations to this JSON file")
     ap.add_argument("--pmc-summary", nargs=4,
