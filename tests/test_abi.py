@@ -91,3 +91,15 @@ def test_binding_constants_match_the_header():
             "SC_MFMA_MIN_ROWS_DOWN", "SC_N_KERNELS"} <= set(mirrored)
     for n in mirrored:
         assert getattr(B, n) == int(defs[n]), n
+
+
+def test_defined_flags_are_accepted_and_need_no_memory():
+    """Both defined flags, alone and together, pass the configuration checks
+    and leave every buffer size unchanged (the overlapped fill and the
+    batch-invariant rows reuse the plain path's buffers)."""
+    base = B.slotcache_query_sizes(_cfg())
+    for flags in (B.SC_FLAG_BATCH_INVARIANT, B.SC_FLAG_OVERLAP_FILL,
+                  B.SC_FLAG_BATCH_INVARIANT | B.SC_FLAG_OVERLAP_FILL):
+        s = B.slotcache_query_sizes(_cfg(flags=flags))
+        for f in ("blob_bytes", "slot_pool_bytes", "state_bytes", "workspace_bytes", "backing_bytes_per_bank"):
+            assert getattr(s, f) == getattr(base, f), (flags, f)
