@@ -67,6 +67,17 @@ def parse():
     return ap.parse_args()
 
 
+def rocprof_duration(src_hash):
+    """The gate/up kernel's rocprofv3 duration over the all-hit timed launches of a
+    profiled bench run, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "dur_gateup_glm_m1.json")
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    return d if d.get("source_sha256") == src_hash else None
+
+
 def pmc_traffic(kernel_key, src_hash):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -288,12 +299,22 @@ def trace_summary(trace_csv, steps_json):
     hit = [timed[i] for i in st["all_hit_timed_steps"]]
     ev = st["gateup_us_events"]
     sp = st["gateup_us_spans"]
-    print(json.dumps({"spans_avg_us_all_hit": round(float(np.mean([sp[i] for i in st["all_hit_timed_steps"]])), 3),
-                      "gateup_launches_in_trace": len(dur), "timed_launches": len(timed),
-                      "all_hit_launches": len(hit),
-                      "rocprof_avg_us_all_hit": round(float(np.mean(hit)), 3),
-                      "events_avg_us_all_hit": round(float(np.mean([ev[i] for i in st["all_hit_timed_steps"]])), 3),
-                      "rocprof_avg_us_all_launches": round(float(np.mean(dur)), 3)}))
+    out = {"spans_avg_us_all_hit": round(float(np.mean([sp[i] for i in st["all_hit_timed_steps"]])), 3),
+           "gateup_launches_in_trace": len(dur), "timed_launches": len(timed),
+           "all_hit_launches": len(hit),
+           "rocprof_avg_us_all_hit": round(float(np.mean(hit)), 3),
+           "events_avg_us_all_hit": round(float(np.mean([ev[i] for i in st["all_hit_timed_steps"]])), 3),
+           "rocprof_avg_us_all_launches": round(float(np.mean(dur)), 3)}
+    print(json.dumps(out))
+    # kept beside the counters: the bench line quotes the rocprofv3 duration of the same
+    # kernel source next to its own measurement
+    rec = dict(out, kernel=KERNEL_NAMES["gateup"], source_sha256=source_hash(),
+               command="rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- "
+                       "python3 -u bench.py --no-cpu-baseline --dump-steps gpurun_out/steps_prof.json; "
+                       "python3 bench.py --trace-summary gpurun_out/prof_bench/run_kernel_trace.csv "
+                       "gpurun_out/steps_prof.json")
+    with open(os.path.join(ROOT, "profiles", "dur_gateup_glm_m1.json"), "w") as f:
+        json.dump(rec, f, indent=1)
 
 
 def prefill(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace):
@@ -551,6 +572,15 @@ def main():
     # the committed counters were taken on the plain gate/up kernel
     traffic = None if a.overlap_fill else pmc_traffic("gateup_glm_m1", src_hash)
     gu_kernel = ("k_fill_gateup<%d> (product blocks)" % H) if a.overlap_fill else KERNEL_NAMES["gateup"]
+    dur = None if a.overlap_fill else rocprof_duration(src_hash)
+    # the same launches in a rocprofv3 trace of this kernel source: its dispatch windows include
+    # the wave launch before the first block starts and the kernel's end after the last
+    # wavefront, which the kernel's own stamps do not
+    duration_check = None if dur is None else {
+        "rocprof_avg_us": dur["rocprof_avg_us_all_hit"], "own_stamps_avg_us": dur["spans_avg_us_all_hit"],
+        "launches": dur["all_hit_launches"],
+        "frac_at_rocprof_duration": round(gateup_bytes / (dur["rocprof_avg_us_all_hit"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "source": "profiles/dur_gateup_glm_m1.json"}
     result = {
         "metric": METRIC,
         "value": round(graph_us, 3),
@@ -593,6 +623,9 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": gateup_bytes, "avg_launch_us": gu,
             "launches": "gate/up kernel on the %d all-hit timed steps" % len(hit_idx),
+            "duration": "mean of the kernel's own execution spans (first block start to last wavefront end, "
+                        "device wall clock)",
+            "rocprof_check": duration_check,
         },
         "down_gemv": {"kernel": KERNEL_NAMES["down"], "achieved_GBs": round(down_bytes / (dn * 1e-6) / 1e9, 1),
                       "avg_launch_us": dn, "algorithmic_bytes_per_launch": down_bytes},
