@@ -433,7 +433,7 @@ def main():
         pmc_summary(*a.pmc_summary)
         return
     if a.gpus != 1:
-        print("bench.py measures one GPU: this build runs the path on a single MI355X "
+        print("bench.py measures one GPU: the decode path runs on a single MI355X "
               "(no collectives); --gpus %d is not supported" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
