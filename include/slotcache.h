@@ -121,10 +121,11 @@ typedef struct {
  * flag.  The trade-off: a step with misses finishes sooner by about the
  * resident experts' gate/up time, but the copy blocks take wave slots from
  * the products, so an all-hit step's gate/up runs slower.  Steps of more than
- * one row are not affected.  With events (moe_layer_decode_ev) the fill
- * events bracket the shared launch and its spans are its copy blocks'; the
- * gate/up events and spans are those of its product blocks; the copied
- * experts' gate/up launch is not timed. */
+ * one row are not affected.  With events (moe_layer_decode_ev) both the
+ * fill and the gate/up events bracket the shared launch; the fill spans are
+ * those of its copy blocks and the gate/up spans those of its product blocks
+ * (slotcache_read_kernel_spans); the copied experts' gate/up launch is not
+ * timed. */
 #define SC_FLAG_OVERLAP_FILL 2u
 
 /* Without SC_FLAG_BATCH_INVARIANT, steps of at least this many rows run the
