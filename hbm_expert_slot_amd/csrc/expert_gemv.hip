@@ -883,9 +883,13 @@ int gemv_blocks(long stages, int cap) {
 // blocks only started once the first ones had finished (about 12 us in) and
 // streamed alone at the end (GLM layer, M=1: 21.2 against 20.6 us).
 constexpr int kGateupBlocks = 768;
-// One block per compute unit keeps 4 MiB of host reads in flight, far more
-// than the host link needs, and leaves the other wave slots to the products.
-constexpr int kFillBlocks = 256;
+// Copy blocks.  Two per compute unit (8 MiB of host reads in flight) move
+// 56.0 GB/s over the host link against 55.5 with one per compute unit (GLM
+// layer, M=1, miss steps; 1 % off the mean step).  A launch that shares its
+// compute units with gate/up products (the overlapped fill) takes one per
+// compute unit, so that the products keep two of their three wave slots.
+constexpr int kFillBlocks = 512;
+constexpr int kFillBlocksShared = 256;
 constexpr int kDownBlocks = 512;
 
 int mr_for(int M) { return M == 1 ? 1 : 2; }
@@ -1031,8 +1035,8 @@ hipError_t launch_fill_gateup(const Shape& sh, const Workspace& W, const float* 
   f.src = W.miss_src;
   f.dst = W.miss_dst;
   f.n16 = (long)(sh.blob / 16);
-  f.span = ev_fill.span_for(kFillBlocks);
-  return sc_launch(fn, dim3(kFillBlocks + blocks), dim3(kGemvThreads), st, ev, f, a, kFillBlocks);
+  f.span = ev_fill.span_for(kFillBlocksShared);
+  return sc_launch(fn, dim3(kFillBlocksShared + blocks), dim3(kGemvThreads), st, ev, f, a, kFillBlocksShared);
 }
 
 hipError_t launch_gateup_filled(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x,
