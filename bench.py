@@ -93,11 +93,21 @@ def pmc_traffic(kernel_key, src_hash):
     return d.get("bytes_per_launch")
 
 
+def code_text(src):
+    """Source text with comments and whitespace runs removed: edits to comments do not
+    change it, edits to code do."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_hash():
+    """Hash of the GEMV kernels' code, the key of the committed counter and duration summaries."""
     import hashlib
     h = hashlib.sha256()
     for f in ("expert_gemv.hip", "internal.h"):
-        h.update(open(os.path.join(ROOT, "hbm_expert_slot_amd", "csrc", f), "rb").read())
+        h.update(code_text(open(os.path.join(ROOT, "hbm_expert_slot_amd", "csrc", f)).read()).encode())
     return h.hexdigest()
 
 

@@ -885,7 +885,7 @@ int gemv_blocks(long stages, int cap) {
 constexpr int kGateupBlocks = 768;
 // Copy blocks.  Two per compute unit (8 MiB of host reads in flight) move
 // 56.0 GB/s over the host link against 55.5 with one per compute unit (GLM
-// layer, M=1, miss steps; 1 % off the mean step).  A launch that shares its
+// layer, M=1, miss steps; 1% off the mean step).  A launch that shares its
 // compute units with gate/up products (the overlapped fill) takes one per
 // compute unit, so that the products keep two of their three wave slots.
 constexpr int kFillBlocks = 512;

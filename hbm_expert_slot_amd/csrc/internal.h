@@ -158,7 +158,8 @@ hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
 // group: -1 for a whole step (the step's misses / all its unique experts),
 // g >= 0 for group g of a staged prefill step.
 hipError_t launch_fill(const Shape& sh, const Workspace& W, int group, hipStream_t st, KEvents ev);
-// mfma: the matrix-core kernels may serve M >= 12 (off: the streaming kernels for every M).
+// mfma: the matrix-core kernels serve M >= SC_MFMA_MIN_ROWS_GATEUP (gate/up) and
+// SC_MFMA_MIN_ROWS_DOWN (down); off: the streaming kernels for every M.
 hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, const uint16_t* x, int M,
                          bool mfma, int group, hipStream_t st, KEvents ev);
 // Overlapped fill of a one-row step (SC_FLAG_OVERLAP_FILL), two launches in
