@@ -225,3 +225,46 @@ def test_overlap_fill_random_layers():
         log("overlapped fill, random layer %d: worst rel L2 %.3g, stats %s" % (i, worst, ov.stats(0)))
         ov.close()
         pl.close()
+
+
+def test_overlap_fill_multi_layer_banks():
+    """Four layers of one handle with 3, 5, 8 and 16 slots over two host
+    backing banks (layer l reads bank l mod 2), one-row steps taken layer by
+    layer: every layer's bookkeeping against its own oracle, outputs against
+    the oracle and bitwise against a handle without the flag."""
+    torch_cuda()
+    from oracle import OracleLayer
+    from gpu_util import OracleBlobs
+    from synth import global_scales
+    cfg = CONFIGS["tiny"]
+    slots, n_banks, steps = [3, 5, 8, 16], 2, 40
+    log("overlapped fill, 4 layers (slots %s) over %d banks, %d steps each" % (slots, n_banks, steps))
+    ov = make_cache(cfg, n_layers=4, slots=slots, max_rows=1, n_banks=n_banks, gs_mode="uniform", overlap_fill=True)
+    pl = make_cache(cfg, n_layers=4, slots=slots, max_rows=1, n_banks=n_banks, gs_mode="uniform")
+    E = cfg.n_experts
+    orcs = [OracleLayer(cfg.hidden, cfg.inter, E, cfg.top_k, S, OracleBlobs(cfg, l % n_banks),
+                        global_scales(cfg, l % n_banks, "uniform")[:E], keep_slot_bytes=False)
+            for l, S in enumerate(slots)]
+    go = [GpuStepper(ov, l) for l in range(4)]
+    gp = [GpuStepper(pl, l) for l in range(4)]
+    rng = np.random.default_rng(77)
+    worst = 0.0
+    for t in range(steps):
+        for l in range(4):
+            z = rng.standard_normal((1, E)).astype(np.float32)
+            z[:, :3] += 1.0
+            x = activations(cfg, 0, 4 * t + l, 1)
+            y, ids, w, byp = go[l].step(z, x)
+            yp, _, _, _ = gp[l].step(z, x)
+            assert np.array_equal(y, yp), (t, l)
+            ev = go[l].new_events()
+            gp[l].new_events()
+            r = _check_step(t, (y, ids, w, byp, ev), orcs[l].decode(z, x), None)
+            worst = max(worst, r)
+    for l in range(4):
+        _check_state(ov, l, orcs[l].state)
+        _check_counters(ov, l, orcs[l].state)
+    log("4 layers: worst rel L2 %.3g, misses per layer %s" % (worst, [ov.stats(l)["misses"] for l in range(4)]))
+    assert ov.stats(0)["evictions"] > 0
+    ov.close()
+    pl.close()
