@@ -35,6 +35,7 @@ sc_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxStateStep = (int64_t)1 << 40;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct LayerOffsets {
@@ -563,8 +564,13 @@ sc_status slotcache_write_state(sc_handle* h, int32_t layer, const int32_t* h_e2
   sc_status st = check_layer(h, layer);
   if (st != SC_OK) return st;
   if (!h_e2s || !h_s2e || !h_key) return fail(SC_E_ARG, "state arrays must be non-NULL");
-  if (step < 0) return fail(SC_E_ARG, "step must be >= 0");
+  // the remap packs (key + 2) above an 11-bit slot index in 64 bits and stamps
+  // keys t * 16k + position: a step below 2^40 keeps both far from overflow
+  if (step < 0 || step >= kMaxStateStep) return fail(SC_E_ARG, "step must be in [0, 2^40)");
   const int E = h->sh.E, S = h->S[layer];
+  // a key the layer could have stamped: -1 (filled, never referenced since) or
+  // t * 16k + position for some earlier step t
+  const int64_t key_end = step * (int64_t)(kCachedRows * h->sh.k);
   for (int e = 0; e < E; ++e) {
     int s = h_e2s[e];
     if (s < -1 || s >= S || (s >= 0 && h_s2e[s] != e))
@@ -575,6 +581,9 @@ sc_status slotcache_write_state(sc_handle* h, int32_t layer, const int32_t* h_e2
     if (e < -1 || e >= E || (e >= 0 && h_e2s[e] != s))
       return fail(SC_E_ARG, "s2e[%d]=%d is not the inverse of e2s", s, e);
     if (e < 0 && h_key[s] != -1) return fail(SC_E_ARG, "empty slot %d must have key -1", s);
+    if (e >= 0 && (h_key[s] < -1 || h_key[s] >= key_end))
+      return fail(SC_E_ARG, "key[%d]=%lld of an occupied slot must be in [-1, step*16*k = %lld)", s,
+                  (long long)h_key[s], (long long)key_end);
   }
   const std::vector<int32_t>& pins = h->pins[layer];
   for (size_t s = 0; s < pins.size(); ++s)

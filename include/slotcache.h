@@ -166,15 +166,30 @@ typedef struct {
   int32_t reserved;
 } sc_event;
 
-/* Sizes of the device buffers the caller must allocate for `cfg`.
- * SC_E_ARG / SC_E_UNSUPPORTED for an invalid or unsupported configuration. */
+/* Sizes of the device buffers the caller must allocate for `cfg`, so that every
+ * device buffer is sized once, up front, before any step runs.  The pages lost
+ * launches to memory that was taken after the budget had been set (page "glm53 -
+ * GLM-5.3-Flash (NVFP4)", section "Context and the KV cap": a cache allocated
+ * after the framework's memory profiling) and to budgets checked in the wrong
+ * units (page "GLM 5.3 Testing: HBM Expert Allocation", section "Five launches,
+ * four failures").  Byte counts are exact (no rounding to a power of two).
+ * Pure: no device or host allocation.  SC_E_ARG / SC_E_UNSUPPORTED for an
+ * invalid or unsupported configuration; *out is left untouched then. */
 SC_API sc_status slotcache_query_sizes(const sc_config* cfg, sc_sizes* out);
 
 /* Binds caller-allocated device buffers (sizes from slotcache_query_sizes,
  * 256-byte aligned), allocates the pinned backing store (n_banks * E * B_e
  * bytes, exact size, device-mapped) and resets every layer to the cold state:
  * all slots empty, keys -1, counters zero, global scales 1.0.  Synchronous.
- * The device buffers must outlive the handle. */
+ * The device buffers must outlive the handle.
+ * Page "GLM 5.3 Testing: HBM Expert Allocation": the per-layer slots and the
+ * pinned backing store are section "What the slot cache is"; pinning at the
+ * exact byte size (a rounding pinned allocator wasted a third of host memory)
+ * is section "Five launches, four failures"; the cache starts empty and is
+ * filled on demand (page "TensorFold GLM-5.3 explained": nothing is resident
+ * for good).  Errors: SC_E_ARG (bad config, NULL or misaligned buffer),
+ * SC_E_HOST_OOM (pinned allocation failed; nothing is kept), SC_E_HIP; *out is
+ * NULL on any error. */
 SC_API sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
                          void* d_workspace, sc_handle** out);
 
@@ -192,7 +207,12 @@ SC_API sc_status slotcache_set_global_scales(sc_handle* h, int32_t bank, const f
  * makes every expert resident (the all-resident layer). */
 SC_API sc_status slotcache_preload(sc_handle* h, int32_t layer);
 
-/* One decode step of `layer` for M rows (1 <= M <= max_rows):
+/* One decode step of `layer` for M rows (1 <= M <= max_rows), the method of
+ * page "GLM 5.3 Testing: HBM Expert Allocation", section "What the slot cache
+ * is" (ids mapped to slots on the device before the expert launch, misses copied
+ * into LRU victims, the expert products reading the same bytes as with every
+ * expert resident, more than 16 rows bypassing, fixed addresses and shapes for
+ * graph capture), with the fp32 combine of its section "A correction first":
  *   d_logits fp32 [M][E], d_x bf16 bits [M][H], d_y fp32 [M][H] (written).
  * Router: per row the k largest logits (ties -> lower expert id, NaN below
  * -inf), weights = softmax over the k chosen logits.  Cached steps (M <= 16
@@ -238,26 +258,45 @@ SC_API sc_status slotcache_pin(sc_handle* h, int32_t layer, const int32_t* h_exp
  * stream of the last step.  SC_E_STATE if that step was not a timed one. */
 SC_API sc_status slotcache_read_kernel_spans(sc_handle* h, double* us_out);
 
-/* Counters of `layer`.  Synchronizes the stream of the last step. */
+/* Counters of `layer`: the hit and miss counts that the pages read from the
+ * engine's periodic cache statistics (page "GB300 GLM 5.3 Testing", section
+ * "Sizing the context window: 256K, measured") and keep as hit/miss logs beside
+ * every speed claim (same page, section "What changed in our policy").
+ * Synchronizes the stream of the last step.  SC_E_DEVICE (with *out filled) when
+ * a device-side check latched an error word on the layer. */
 SC_API sc_status slotcache_stats(sc_handle* h, int32_t layer, sc_stats* out);
 
 /* Slot map and LRU clock of `layer` (synchronizes): h_e2s int32[E] (slot or
  * -1), h_s2e int32[S] (expert or -1), h_key int64[S] (-1 = empty), h_step
- * (step counter).  Any output pointer may be NULL. */
+ * (step counter).  Any output pointer may be NULL.  The slots are only a cache:
+ * the backing store keeps the only full copy of every expert (page "TensorFold
+ * GLM-5.3 explained"), so this state plus the backing store is a complete
+ * checkpoint of the layer, and it is what the pages' "no stale slots" parity
+ * check inspects (page "GB300 GLM 5.3 Testing", section "What changed in our
+ * policy"). */
 SC_API sc_status slotcache_read_state(sc_handle* h, int32_t layer, int32_t* h_e2s, int32_t* h_s2e,
                                int64_t* h_key, int64_t* h_step);
 
-/* Restores a state read by slotcache_read_state (checkpoint / resume): checks
- * that the maps are mutually inverse, copies the resident experts' blobs from
- * the backing store into their slots and writes maps, keys and step counter.
- * Counters and the event ring are left as they are.  Synchronous. */
+/* Restores a state read by slotcache_read_state (checkpoint / resume; the
+ * backing store keeps the only full copy, page "TensorFold GLM-5.3 explained"):
+ * copies the resident experts' blobs from the backing store into their slots
+ * and writes maps, keys and step counter.  Counters and the event ring are left
+ * as they are.  Synchronous.  SC_E_ARG, with nothing written, unless: the maps
+ * are mutually inverse; empty slots have key -1; every occupied slot's key is a
+ * clock value the layer could have stamped, -1 <= key < step * 16 * k (-1: never
+ * referenced since it was filled); 0 <= step < 2^40; pinned slots keep their
+ * experts. */
 SC_API sc_status slotcache_write_state(sc_handle* h, int32_t layer, const int32_t* h_e2s,
                                 const int32_t* h_s2e, const int64_t* h_key, int64_t step);
 
-/* Miss events of `layer`, oldest first (synchronizes).  Copies up to `cap`
- * records of the most recent min(total, event_capacity) into h_buf; *n_out =
- * records copied, *total = events ever logged (total > event_capacity means
- * the ring wrapped). */
+/* Miss events of `layer`, oldest first (synchronizes): the per-miss record
+ * (step, expert in, slot, expert evicted) behind the pages' hit/miss logs (page
+ * "GB300 GLM 5.3 Testing", section "What changed in our policy") and their
+ * bit-exact churn comparisons (page "GLM 5.3 Testing: HBM Expert Allocation",
+ * section "The build").  Copies up to `cap` records of the most recent
+ * min(total, event_capacity) into h_buf; *n_out = records copied, *total =
+ * events ever logged (total > event_capacity means the ring wrapped).  SC_E_ARG
+ * if h_buf is NULL while records are available and cap > 0. */
 SC_API sc_status slotcache_read_events(sc_handle* h, int32_t layer, sc_event* h_buf, size_t cap,
                                 size_t* n_out, uint64_t* total);
 

@@ -10,6 +10,8 @@ from .gen import (
     e4m3_bits_rne,
     expert_blob,
     expert_blobs,
+    probe_blob,
+    probe_column,
     global_scales,
     activations,
     routing_trace,
@@ -18,5 +20,5 @@ from .gen import (
 __all__ = [
     "CONFIGS", "WorkloadConfig", "blob_parts", "blob_bytes", "rows_at_step",
     "bf16_bits_from_f32", "e4m3_bits_rne", "expert_blob", "expert_blobs",
-    "global_scales", "activations", "routing_trace",
+    "global_scales", "activations", "routing_trace", "probe_blob", "probe_column",
 ]

@@ -148,3 +148,51 @@ def routing_trace(cfg: WorkloadConfig, layer: int = 0, steps=None):
                 z[m, share] += 20.0
         out[t, :M] = z.astype(np.float32)
     return out, rows
+
+
+# E2M1 code of 1.0 (exponent field 1, mantissa 0) and E4M3 byte of 1.0 (exponent field 7).
+_E2M1_ONE = 0x2
+_E4M3_ONE = 0x38
+
+
+def probe_column(cfg: WorkloadConfig, expert: int) -> int:
+    """The intermediate index that a "one_column" probe blob of `expert` keeps."""
+    return (expert * 37 + 5) % cfg.inter
+
+
+def probe_blob(cfg: WorkloadConfig, bank: int, expert: int, mode: str) -> np.ndarray:
+    """A seeded random blob with one matrix replaced by a structured one, so that a
+    step's output exposes single weights instead of a long dot product.
+
+    "select_h": the down matrix is a selection matrix: row r holds 1.0 at column
+      r mod I and zero elsewhere (every block scale 1.0).  With one pick per row
+      and a unit global scale the output row repeats the expert's intermediate
+      vector.
+    "one_column": every up row is zero except row probe_column(cfg, expert), so
+      the intermediate vector is zero except at that index and the output is one
+      column of the down matrix times one intermediate value.
+    """
+    out = expert_blob(cfg, bank, expert)
+    H, I = cfg.hidden, cfg.inter
+    parts = dict()
+    off = 0
+    for name, n in blob_parts(H, I):
+        parts[name] = (off, n)
+        off += n
+    if mode == "select_h":
+        o, n = parts["w2_codes"]
+        codes = np.zeros((H, I), dtype=np.uint8)
+        codes[np.arange(H), np.arange(H) % I] = _E2M1_ONE
+        out[o:o + n] = (codes[:, 0::2] | (codes[:, 1::2] << 4)).reshape(-1)
+        o, n = parts["w2_scales"]
+        out[o:o + n] = _E4M3_ONE
+    elif mode == "one_column":
+        o, n = parts["w13_codes"]
+        w13 = out[o:o + n].reshape(2 * I, H // 2)
+        keep = I + probe_column(cfg, expert)
+        row = w13[keep].copy()
+        w13[I:] = 0
+        w13[keep] = row
+    else:
+        raise ValueError(mode)
+    return out

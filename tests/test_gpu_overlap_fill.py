@@ -8,7 +8,7 @@ import pytest
 
 from synth import CONFIGS, WorkloadConfig, activations, routing_trace
 
-from gpu_util import GpuStepper, log, make_cache, rel_l2, torch_cuda
+from gpu_util import GpuStepper, check_output, log, make_cache, torch_cuda
 from test_gpu_parity import (Y_TOL, _check_counters, _check_slots_hold_their_experts, _check_state,
                              _check_step, _oracle_layer)
 
@@ -173,7 +173,7 @@ def test_overlap_fill_graph_replay_under_churn():
         g.replay()
         torch.cuda.synchronize()
         y_o, rec, ids_o, w_o = orc.decode(logits[t, :1], xb)
-        assert rel_l2(y.cpu().numpy(), y_o) <= Y_TOL, t
+        check_output(y.cpu().numpy(), y_o, t)
         assert [tuple(e[1:]) for e in stepper.new_events()] == rec.events, t
         _check_state(sc, 0, orc.state)
         _ = (y * 2).sum().item()

@@ -11,11 +11,10 @@ import pytest
 from oracle import OracleLayer, route
 from synth import CONFIGS, WorkloadConfig, activations, global_scales, routing_trace
 
-from gpu_util import GpuStepper, OracleBlobs, log, make_cache, rel_l2, torch_cuda
+from gpu_util import Y_TOL, GpuStepper, OracleBlobs, check_output, log, make_cache, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 1e-3
 W_TOL = 1e-6
 GOLD = os.path.join(os.path.dirname(__file__), "golden", "lru_hand_trace.json")
 
@@ -35,9 +34,7 @@ def _check_step(t, gpu_out, orc, rec_events, want_y=True):
     assert [tuple(e[1:]) for e in ev_gpu] == rec.events, (t, ev_gpu, rec.events)
     assert all(e[0] == rec.step for e in ev_gpu)
     if want_y:
-        r = rel_l2(y_gpu, y_o)
-        assert r <= Y_TOL, (t, r)
-        return r
+        return check_output(y_gpu, y_o, t)
     return None
 
 
@@ -239,7 +236,7 @@ def test_graph_replay_under_churn():
         g.replay()
         torch.cuda.synchronize()
         y_o, rec, ids_o, w_o = orc.decode(logits[t, :1], xb)
-        assert rel_l2(y.cpu().numpy(), y_o) <= Y_TOL, t
+        check_output(y.cpu().numpy(), y_o, t)
         assert [tuple(e[1:]) for e in stepper.new_events()] == rec.events, t
         _check_state(sc, 0, orc.state)
         _ = (y * 2).sum().item()     # unrelated eager work between replays
@@ -269,6 +266,40 @@ def test_checkpoint_resume_matches_a_continuous_run():
         assert np.array_equal(u, v)
     a.close()
     b.close()
+
+
+def test_write_state_rejects_keys_the_layer_cannot_have_stamped():
+    """Occupied slots' keys must lie in [-1, step*16*k) and the step in [0, 2^40): the remap
+    orders victims by packing (key + 2) above the slot index, so keys outside that range
+    would reorder victims against the oracle's signed (key, slot) order.  A rejected
+    state changes nothing."""
+    from hbm_expert_slot_amd import binding as B
+    torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("write_state key checks: tiny")
+    sc = make_cache(cfg)
+    logits, _ = routing_trace(cfg, 0)
+    g = GpuStepper(sc)
+    for t in range(10):
+        g.step(logits[t, :1], activations(cfg, 0, t, 1))
+    e2s, s2e, key, step = sc.read_state(0)
+    occ = int(np.nonzero(s2e >= 0)[0][0])
+    end = step * 16 * cfg.top_k
+    for bad_key, bad_step in ((-2, step), (end, step), (1 << 62, step), (-(1 << 62), step), (0, 1 << 40),
+                              (0, -1)):
+        k2 = key.copy()
+        k2[occ] = bad_key
+        with pytest.raises(B.SlotCacheError) as ei:
+            sc.write_state(0, e2s, s2e, k2, bad_step)
+        assert ei.value.status == B.SC_E_ARG, (bad_key, bad_step)
+        for u, v in zip(sc.read_state(0), (e2s, s2e, key, step)):
+            assert np.array_equal(u, v)
+    # the limits themselves are accepted
+    for ok_key in (-1, end - 1):
+        k2 = key.copy()
+        k2[occ] = ok_key
+        sc.write_state(0, e2s, s2e, k2, step)
+    sc.close()
 
 
 @pytest.mark.timeout(600)
@@ -540,8 +571,7 @@ def test_prefill_groups_match_in_place_reads(shape):
         if M > 16:
             assert rec.bypass
         if want_y:
-            r = rel_l2(ys[Gs[-1]], y_o)
-            assert r <= Y_TOL, (t, M, r)
+            r = check_output(ys[Gs[-1]], y_o, (t, M))
             worst = max(worst, r)
     for G, sc in caches.items():
         _check_state(sc, 0, orc.state)
@@ -705,7 +735,7 @@ def test_graph_replay_of_multi_row_and_staged_prefill_steps():
         graphs[M].replay()
         torch.cuda.synchronize()
         y_o, rec, ids_o, w_o = orc.decode(zh, xh)
-        assert rel_l2(y.cpu().numpy(), y_o) <= Y_TOL, (t, M)
+        check_output(y.cpu().numpy(), y_o, (t, M))
         if M > 16:
             assert rec.bypass
         assert [tuple(e[1:]) for e in stepper.new_events()] == rec.events, (t, M)
