@@ -24,13 +24,14 @@ SC_MFMA_MIN_ROWS_GATEUP = 3
 SC_MFMA_MIN_ROWS_DOWN = 3
 SC_N_KERNELS = 5
 SC_N_EVENTS = 2 * SC_N_KERNELS
+SC_STATIC_SCRATCH_BYTES = 16777216
 
 EXPORTED = (
     "slotcache_query_sizes", "slotcache_init", "slotcache_backing", "slotcache_set_global_scales",
     "slotcache_preload", "moe_layer_decode", "moe_layer_decode_ev", "slotcache_stats",
     "slotcache_read_state", "slotcache_write_state", "slotcache_read_events",
     "slotcache_read_routing", "slotcache_read_kernel_spans", "slotcache_pin", "slotcache_last_error",
-    "slotcache_destroy",
+    "slotcache_destroy", "moe_layer_decode_static",
 )
 
 
@@ -89,6 +90,7 @@ def lib():
             "slotcache_preload": [P, i32],
             "moe_layer_decode": [P, i32, P, P, i32, P, P],
             "moe_layer_decode_ev": [P, i32, P, P, i32, P, P, P],
+            "moe_layer_decode_static": [P, i32, P, P, i32, P, P],
             "slotcache_stats": [P, i32, ctypes.POINTER(sc_stats)],
             "slotcache_read_state": [P, i32, P, P, P, P],
             "slotcache_write_state": [P, i32, P, P, P, i64],
@@ -152,6 +154,10 @@ def slotcache_preload(h, layer):
 
 def moe_layer_decode(h, layer, d_logits, d_x, M, d_y, stream):
     _check(lib().moe_layer_decode(h, layer, d_logits, d_x, M, d_y, stream))
+
+
+def moe_layer_decode_static(h, layer, d_logits, d_x, M, d_y, stream):
+    _check(lib().moe_layer_decode_static(h, layer, d_logits, d_x, M, d_y, stream))
 
 
 def moe_layer_decode_ev(h, layer, d_logits, d_x, M, d_y, stream, events):

@@ -11,10 +11,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 using namespace sc;
+
+// Per-call scratch of moe_layer_decode_static, for callers that cannot
+// allocate: one fixed array per GPU, held until the process ends.  Host code
+// never uses this name as an address (on the host it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, looked up
+// once per device (static_scratch below).
+static __device__ __align__(256) uint8_t scratch[SC_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -134,6 +142,60 @@ sc_status check_config(const sc_config* c) {
 
 int ev_cap_of(const sc_config* c) { return c->event_capacity ? c->event_capacity : 4096; }
 
+// Workspace view of a scratch region laid out by `o`.
+Workspace bind_workspace(uint8_t* ws, const WsOffsets& o, int stage_n) {
+  Workspace W;
+  W.hdr = reinterpret_cast<int32_t*>(ws + o.hdr);
+  W.pick_expert = reinterpret_cast<int32_t*>(ws + o.pick_expert);
+  W.pick_w = reinterpret_cast<float*>(ws + o.pick_w);
+  W.pick_u = reinterpret_cast<int32_t*>(ws + o.pick_u);
+  W.uniq_expert = reinterpret_cast<int32_t*>(ws + o.uniq_expert);
+  W.uniq_ptr = reinterpret_cast<const uint8_t**>(ws + o.uniq_ptr);
+  W.uniq_off = reinterpret_cast<int32_t*>(ws + o.uniq_off);
+  W.uniq_picks = reinterpret_cast<int32_t*>(ws + o.uniq_picks);
+  W.miss_src = reinterpret_cast<const uint8_t**>(ws + o.miss_src);
+  W.miss_dst = reinterpret_cast<uint8_t**>(ws + o.miss_dst);
+  W.h = reinterpret_cast<float*>(ws + o.h);
+  W.part = reinterpret_cast<float*>(ws + o.part);
+  W.uniq_order = reinterpret_cast<int32_t*>(ws + o.uniq_order);
+  W.stage_n = stage_n;
+  W.stage = stage_n > 0 ? ws + o.stage : nullptr;
+  return W;
+}
+
+// Layout of the static scratch for a configuration: steps of at most
+// SC_BYPASS_ROWS rows, no prefill staging area.
+WsOffsets static_offsets(const sc_config* c) {
+  const int rows = c->max_rows < kCachedRows ? c->max_rows : kCachedRows;
+  return ws_offsets(rows * c->top_k, c->hidden, c->inter, rows, 0, 0);
+}
+
+// Device address of `scratch` on each device, looked up once per device (with
+// that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices];
+
+sc_status static_scratch(int dev, uint8_t** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0 || dev >= kMaxDevices) return fail(SC_E_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(SC_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    // set-up, not a step: the array starts out zeroed once, before any call uses it
+    e = hipMemset(p, 0, SC_STATIC_SCRATCH_BYTES);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipMemset (static scratch)");
+    g_scratch[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return SC_OK;
+}
+
 }  // namespace
 
 struct sc_handle {
@@ -160,6 +222,12 @@ struct sc_handle {
   uint64_t* d_span;                 // [SC_N_KERNELS][span_cap][kSpanSlots]
   int span_cap;
   int clock_khz;                    // wall clock rate of the span stamps
+  Workspace last_W;                 // workspace of the last step (read_routing reads it)
+  int device;                       // device the handle was set up on
+  bool static_ok;                   // moe_layer_decode_static can run (scratch found and large enough)
+  size_t static_need;               // bytes of static scratch the configuration needs
+  std::string static_err;           // why it cannot, otherwise
+  Workspace W_static;               // the static scratch laid out for this configuration
 };
 
 namespace {
@@ -304,32 +372,35 @@ sc_status slotcache_init(const sc_config* cfg, void* d_slot_pool, void* d_state,
     }
     h->bank_dev.push_back(d);
   }
-  uint8_t* ws = h->d_ws;
   const WsOffsets& o = h->wo;
-  h->W.hdr = reinterpret_cast<int32_t*>(ws + o.hdr);
-  h->W.pick_expert = reinterpret_cast<int32_t*>(ws + o.pick_expert);
-  h->W.pick_w = reinterpret_cast<float*>(ws + o.pick_w);
-  h->W.pick_u = reinterpret_cast<int32_t*>(ws + o.pick_u);
-  h->W.uniq_expert = reinterpret_cast<int32_t*>(ws + o.uniq_expert);
-  h->W.uniq_ptr = reinterpret_cast<const uint8_t**>(ws + o.uniq_ptr);
-  h->W.uniq_off = reinterpret_cast<int32_t*>(ws + o.uniq_off);
-  h->W.uniq_picks = reinterpret_cast<int32_t*>(ws + o.uniq_picks);
-  h->W.miss_src = reinterpret_cast<const uint8_t**>(ws + o.miss_src);
-  h->W.miss_dst = reinterpret_cast<uint8_t**>(ws + o.miss_dst);
-  h->W.h = reinterpret_cast<float*>(ws + o.h);
-  h->W.part = reinterpret_cast<float*>(ws + o.part);
-  h->W.uniq_order = reinterpret_cast<int32_t*>(ws + o.uniq_order);
-  h->W.stage_n = stage_experts(cfg);
-  h->W.stage = h->W.stage_n > 0 ? ws + o.stage : nullptr;
-  h->d_span = reinterpret_cast<uint64_t*>(ws + o.span);
+  h->W = bind_workspace(h->d_ws, o, stage_experts(cfg));
+  h->last_W = h->W;
+  h->d_span = reinterpret_cast<uint64_t*>(h->d_ws + o.span);
   h->span_cap = span_blocks(cfg->max_rows, cfg->hidden);
   h->timed = false;
   h->clock_khz = 0;
+  h->device = 0;
+  if (hipGetDevice(&h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&h->clock_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess)
+    (void)hipGetLastError();
+  // the static scratch of this device (moe_layer_decode_static); a failure here
+  // only disables that entry point, which then reports it
   {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&h->clock_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
-      (void)hipGetLastError();
+    const WsOffsets so = static_offsets(cfg);
+    h->static_need = so.end;
+    h->static_ok = false;
+    uint8_t* base = nullptr;
+    if (so.end > (size_t)SC_STATIC_SCRATCH_BYTES) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "the configuration needs %zu bytes of per-call scratch, the static array holds %zu",
+               so.end, (size_t)SC_STATIC_SCRATCH_BYTES);
+      h->static_err = buf;
+    } else if (static_scratch(h->device, &base) != SC_OK) {
+      h->static_err = g_err;
+    } else {
+      h->W_static = bind_workspace(base, so, 0);
+      h->static_ok = true;
+    }
   }
 
   // Cold state: every slot empty, keys -1, counters and rings zero, gs = 1.
@@ -434,12 +505,20 @@ sc_status slotcache_pin(sc_handle* h, int32_t layer, const int32_t* h_experts, i
   return SC_OK;
 }
 
-sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
-                              int32_t M, float* d_y, void* stream, void* const* events) {
+namespace {
+
+sc_status check_step(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x, int32_t M,
+                     float* d_y) {
   sc_status st = check_layer(h, layer);
   if (st != SC_OK) return st;
   if (M < 1 || M > h->cfg.max_rows) return fail(SC_E_ARG, "M=%d must be in [1, %d]", M, h->cfg.max_rows);
   if (!d_logits || !d_x || !d_y) return fail(SC_E_ARG, "logits, x and y must be non-NULL");
+  return SC_OK;
+}
+
+// Enqueues one step whose per-call scratch is `W` (arguments already checked).
+sc_status enqueue_step(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x, int32_t M,
+                       float* d_y, void* stream, void* const* events, const Workspace& W) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   LayerDev L = layer_dev(h, layer);
   hipError_t e = hipSuccess;
@@ -454,41 +533,62 @@ sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits
     return k;
   };
   const bool mfma = !(h->cfg.flags & SC_FLAG_BATCH_INVARIANT);
-  e = launch_route(h->sh, L, h->W, d_logits, M, s, kev(0));
+  e = launch_route(h->sh, L, W, d_logits, M, s, kev(0));
   if (M == 1 && (h->cfg.flags & SC_FLAG_OVERLAP_FILL)) {
     // the copy shares a launch with the resident experts' gate/up; the copied
     // experts' gate/up runs after it
     KEvents fev = kev(1);
     if (e == hipSuccess && fev.start) e = hipEventRecord(fev.start, s);
-    if (e == hipSuccess) e = launch_fill_gateup(h->sh, h->W, L.gs, d_x, s, fev, kev(2));
+    if (e == hipSuccess) e = launch_fill_gateup(h->sh, W, L.gs, d_x, s, fev, kev(2));
     if (e == hipSuccess && fev.stop) e = hipEventRecord(fev.stop, s);
-    if (e == hipSuccess) e = launch_gateup_filled(h->sh, h->W, L.gs, d_x, s);
-    if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, -1, s, kev(3));
-  } else if (!staged_step(h->W, M)) {
-    if (e == hipSuccess) e = launch_fill(h->sh, h->W, -1, s, kev(1));
-    if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, -1, s, kev(2));
-    if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, -1, s, kev(3));
+    if (e == hipSuccess) e = launch_gateup_filled(h->sh, W, L.gs, d_x, s);
+    if (e == hipSuccess) e = launch_down(h->sh, W, L.gs, M, mfma, -1, s, kev(3));
+  } else if (!staged_step(W, M)) {
+    if (e == hipSuccess) e = launch_fill(h->sh, W, -1, s, kev(1));
+    if (e == hipSuccess) e = launch_gateup(h->sh, W, L.gs, d_x, M, mfma, -1, s, kev(2));
+    if (e == hipSuccess) e = launch_down(h->sh, W, L.gs, M, mfma, -1, s, kev(3));
   } else {
     // prefill groups: copy G experts into staging, compute them, next group
-    const int ng = stage_groups(h->W, M, h->sh.k, h->sh.E);
+    const int ng = stage_groups(W, M, h->sh.k, h->sh.E);
     for (int g = 0; g < ng && e == hipSuccess; ++g) {
       auto gev = [&](int i) { return g == 0 ? kev(i) : KEvents(); };
-      e = launch_fill(h->sh, h->W, g, s, gev(1));
-      if (e == hipSuccess) e = launch_gateup(h->sh, h->W, L.gs, d_x, M, mfma, g, s, gev(2));
-      if (e == hipSuccess) e = launch_down(h->sh, h->W, L.gs, M, mfma, g, s, gev(3));
+      e = launch_fill(h->sh, W, g, s, gev(1));
+      if (e == hipSuccess) e = launch_gateup(h->sh, W, L.gs, d_x, M, mfma, g, s, gev(2));
+      if (e == hipSuccess) e = launch_down(h->sh, W, L.gs, M, mfma, g, s, gev(3));
     }
   }
-  if (e == hipSuccess) e = launch_combine(h->sh, h->W, d_y, M, s, kev(4));
+  if (e == hipSuccess) e = launch_combine(h->sh, W, d_y, M, s, kev(4));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   h->last_stream = s;
   h->stepped = true;
   h->timed = events != nullptr;
+  h->last_W = W;
   return SC_OK;
+}
+
+}  // namespace
+
+sc_status moe_layer_decode_ev(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
+                              int32_t M, float* d_y, void* stream, void* const* events) {
+  sc_status st = check_step(h, layer, d_logits, d_x, M, d_y);
+  if (st != SC_OK) return st;
+  return enqueue_step(h, layer, d_logits, d_x, M, d_y, stream, events, h->W);
 }
 
 sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
                            int32_t M, float* d_y, void* stream) {
   return moe_layer_decode_ev(h, layer, d_logits, d_x, M, d_y, stream, nullptr);
+}
+
+sc_status moe_layer_decode_static(sc_handle* h, int32_t layer, const float* d_logits, const uint16_t* d_x,
+                                  int32_t M, float* d_y, void* stream) {
+  sc_status st = check_step(h, layer, d_logits, d_x, M, d_y);
+  if (st != SC_OK) return st;
+  if (M > kCachedRows)
+    return fail(SC_E_ARG, "M=%d: moe_layer_decode_static takes at most %d rows (prefill chunks stage through the "
+                "caller's workspace)", M, kCachedRows);
+  if (!h->static_ok) return fail(SC_E_ARG, "moe_layer_decode_static: %s", h->static_err.c_str());
+  return enqueue_step(h, layer, d_logits, d_x, M, d_y, stream, nullptr, h->W_static);
 }
 
 sc_status slotcache_read_kernel_spans(sc_handle* h, double* us_out) {
@@ -632,11 +732,12 @@ sc_status slotcache_read_routing(sc_handle* h, int32_t* h_ids, float* h_w, int32
   sc_status st = sync_last(h);
   if (st != SC_OK) return st;
   int32_t hdr[H_WORDS];
-  hipError_t e = hipMemcpy(hdr, h->W.hdr, sizeof hdr, hipMemcpyDeviceToHost);
+  const Workspace& W = h->last_W;
+  hipError_t e = hipMemcpy(hdr, W.hdr, sizeof hdr, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (hdr)");
   const int M = hdr[H_ROWS], P = M * h->sh.k;
-  if (h_ids && e == hipSuccess) e = hipMemcpy(h_ids, h->W.pick_expert, (size_t)P * 4, hipMemcpyDeviceToHost);
-  if (h_w && e == hipSuccess) e = hipMemcpy(h_w, h->W.pick_w, (size_t)P * 4, hipMemcpyDeviceToHost);
+  if (h_ids && e == hipSuccess) e = hipMemcpy(h_ids, W.pick_expert, (size_t)P * 4, hipMemcpyDeviceToHost);
+  if (h_w && e == hipSuccess) e = hipMemcpy(h_w, W.pick_w, (size_t)P * 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpy (routing)");
   if (M_out) *M_out = M;
   if (bypass) *bypass = hdr[H_BYPASS];

@@ -225,6 +225,32 @@ SC_API sc_status slotcache_preload(sc_handle* h, int32_t layer);
 SC_API sc_status moe_layer_decode(sc_handle* h, int32_t layer, const float* d_logits,
                            const uint16_t* d_x, int32_t M, float* d_y, void* stream);
 
+/* Bytes of the library's static per-call scratch on each GPU (see
+ * moe_layer_decode_static). */
+#define SC_STATIC_SCRATCH_BYTES 16777216
+
+/* moe_layer_decode for callers that cannot allocate: code under HIP graph
+ * capture that must not touch an allocator, tight serving loops, harnesses
+ * that forbid allocation.  The step's per-call scratch (routing lists, pick
+ * grouping, h, per-pick down outputs) comes from a fixed device array of the
+ * library, SC_STATIC_SCRATCH_BYTES per GPU, set up by slotcache_init on the
+ * handle's device and held until the process ends, instead of the workspace
+ * bound to the handle.  The caller still passes logits, x and y, and the
+ * handle's slots and state are used as by moe_layer_decode; the results are
+ * the same bits.  The call allocates nothing, host or device.
+ * Every call on a GPU shares that GPU's array and leaves its contents behind
+ * (each step writes every scratch word it reads before reading it, so nothing
+ * needs clearing): calls that can overlap on one GPU -- streams not ordered
+ * with each other, from this or any other handle -- race on it and must not
+ * be issued.  slotcache_read_routing reads the array after such a step.
+ * Errors (SC_E_ARG, nothing enqueued): the arguments of moe_layer_decode;
+ * M > SC_BYPASS_ROWS (a prefill chunk needs the caller's workspace and its
+ * staging area); a configuration whose per-call scratch for
+ * min(max_rows, SC_BYPASS_ROWS) rows exceeds SC_STATIC_SCRATCH_BYTES (the
+ * message gives both sizes); the array could not be set up at init. */
+SC_API sc_status moe_layer_decode_static(sc_handle* h, int32_t layer, const float* d_logits,
+                                         const uint16_t* d_x, int32_t M, float* d_y, void* stream);
+
 /* Kernels of one step, for per-kernel timing: routing+remap, miss fill,
  * gate/up, down, combine. */
 #define SC_N_KERNELS 5
