@@ -340,17 +340,21 @@ def test_glm_drafted_rounds_and_prefill_bypass():
 
 
 def test_timed_entry_point_matches_the_plain_one():
-    """moe_layer_decode_ev (per-kernel start/stop events and execution stamps) computes the same step."""
+    """moe_layer_decode_ev (per-kernel start/stop events and execution stamps) computes the same step,
+    on one-row and four-row (matrix-core) steps."""
     torch = torch_cuda()
     from hbm_expert_slot_amd import binding as B
     cfg = CONFIGS["tiny"]
-    log("timed entry point vs plain: tiny, 24 steps")
-    a, b = make_cache(cfg), make_cache(cfg)
+    log("timed entry point vs plain: tiny, 24 steps of 1 and 4 rows")
+    a, b = make_cache(cfg, max_rows=4), make_cache(cfg, max_rows=4)
     logits, _ = routing_trace(cfg, 0)
+    rng = np.random.default_rng(5)
     for t in range(24):
-        z = torch.from_numpy(logits[t, :1]).cuda()
-        x = torch.from_numpy(activations(cfg, 0, t, 1).view(np.int16)).cuda()
-        ya = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
+        M = 4 if t % 3 == 2 else 1
+        zt = logits[t, :1] if M == 1 else rng.standard_normal((M, cfg.n_experts)).astype(np.float32)
+        z = torch.from_numpy(np.ascontiguousarray(zt)).cuda()
+        x = torch.from_numpy(activations(cfg, 0, t, M).view(np.int16)).cuda()
+        ya = torch.empty((M, cfg.hidden), dtype=torch.float32, device="cuda")
         yb = torch.empty_like(ya)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(B.SC_N_EVENTS)]
         for ev in evs:
@@ -363,7 +367,7 @@ def test_timed_entry_point_matches_the_plain_one():
         assert all(v >= 0 for v in ev_ms)
         # the kernels' own start/end stamps: positive, and inside the event brackets
         spans = b.kernel_spans()
-        assert all(0 < s_us <= 1e3 * e_ms + 1.0 for s_us, e_ms in zip(spans, ev_ms)), (spans, ev_ms)
+        assert all(0 < s_us <= 1e3 * e_ms + 1.0 for s_us, e_ms in zip(spans, ev_ms)), (M, spans, ev_ms)
     with pytest.raises(B.SlotCacheError):
         a.kernel_spans()          # a's steps were not timed
     for u, v in zip(a.read_state(0), b.read_state(0)):
