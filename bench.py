@@ -581,7 +581,7 @@ def stack_workload(a, torch, env):
     out = {
         "workload": cfg.description,
         "us_per_layer_step": round(ms * 1e3 / n_ls, 2), "timed_layer_steps": n_ls,
-        "warmup": "%d cache warm-up + %d steps, every layer" % (CW, W),
+        "untimed": "%d cache warm-up + %d warmup steps, every layer" % (CW, W),
         "hit_rate": round(d["hits"] / d["lookups"], 4) if d["lookups"] else None,
         "misses_per_layer_step": round(d["misses"] / n_ls, 3),
         "unique_experts_per_layer_step": round(d["lookups"] / max(1, n_ls - d["bypass_steps"]), 2),
