@@ -100,3 +100,46 @@ def test_static_entry_point_limits():
     B.moe_layer_decode(sc.h, 0, z.data_ptr(), x.data_ptr(), 1, y.data_ptr(), s)   # the workspace path still runs
     assert sc.stats(0)["steps"] == 1
     sc.close()
+
+
+def test_static_entry_point_under_graph_capture():
+    """The use it is for: steps captured into a HIP graph through the static entry point,
+    replayed three times, each replay checked against the same steps run eagerly through
+    the workspace entry point on a second handle (outputs, routing state, counters)."""
+    from hbm_expert_slot_amd import binding as B
+    torch = torch_cuda()
+    cfg = CONFIGS["tiny"]
+    log("static scratch entry point under graph capture: tiny, 6 steps of 1-4 rows, 3 replays")
+    a, b = _pair(cfg, 4, cfg.slots)
+    rng = np.random.default_rng(29)
+    rows = [1, 4, 2, 1, 3, 1]
+    zs = [torch.from_numpy(rng.standard_normal((M, cfg.n_experts)).astype(np.float32)).cuda() for M in rows]
+    xs = [torch.from_numpy(activations(cfg, 0, t, M).view(np.int16)).cuda() for t, M in enumerate(rows)]
+    ya = [torch.zeros((M, cfg.hidden), dtype=torch.float32, device="cuda") for M in rows]
+    yb = [torch.zeros((M, cfg.hidden), dtype=torch.float32, device="cuda") for M in rows]
+    gstream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gstream):
+        g.capture_begin()
+        for t, M in enumerate(rows):
+            B.moe_layer_decode_static(a.h, 0, zs[t].data_ptr(), xs[t].data_ptr(), M, ya[t].data_ptr(),
+                                      gstream.cuda_stream)
+        g.capture_end()
+    torch.cuda.synchronize()
+    assert a.stats(0)["steps"] == 0            # capture enqueues nothing
+    s = torch.cuda.current_stream().cuda_stream
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for t, M in enumerate(rows):
+            B.moe_layer_decode(b.h, 0, zs[t].data_ptr(), xs[t].data_ptr(), M, yb[t].data_ptr(), s)
+        torch.cuda.synchronize()
+        for t in range(len(rows)):
+            assert torch.equal(ya[t], yb[t]), (rep, t)
+        for u, v in zip(a.read_state(0), b.read_state(0)):
+            assert np.array_equal(u, v), rep
+        assert a.stats(0) == b.stats(0), rep
+    assert b.stats(0)["misses"] > 0
+    a.close()
+    b.close()
