@@ -22,6 +22,8 @@
 // block sum; the fp32 global scale multiplies the row sum.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace sc {
 namespace {
 
@@ -298,10 +300,55 @@ struct Gemv {
     }
   }
 
+  // seg_dot_f32 with the codes already widened: w[4 * dw + sel] from dword dw
+  __device__ static __forceinline__ float blocks_dot_f32(const f32x2 (&w)[16], float s0, float s1, const float* hv) {
+    float bsum[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc = fmaf(w[blk * 8 + e].x, hv[2 * (blk * 8 + e)], acc);
+        acc = fmaf(w[blk * 8 + e].y, hv[2 * (blk * 8 + e) + 1], acc);
+      }
+      bsum[blk] = acc;
+    }
+    return fmaf(bsum[1], s1, bsum[0] * s0);
+  }
+
   __device__ static __forceinline__ void process(const Buf& b, const uint32_t (&opw)[MR][NSEG][OPW],
                                                  const int (&pk)[MR], int nc, int i, int n, int base,
                                                  int stride, int lane, int rsub, float gs, const GemvArgs& a) {
     float v0[NV], v1[NV];
+    if constexpr (!GATEUP && MR > 1) {
+      // down with several picks: each row's codes are widened once and serve
+      // every pick (same products and order as seg_dot_f32)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) v0[e] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int c = 0; c < NSEG; ++c) {
+          const uint32_t d[4] = {b.q[j][0][c].x, b.q[j][0][c].y, b.q[j][0][c].z, b.q[j][0][c].w};
+          f32x2 w[16];
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            f32x2 t[4];
+            fp4x8_f32(d[dw], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[4 * dw + e] = t[e];
+          }
+          const float s0 = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
+          const float s1 = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
+#pragma unroll
+          for (int mi = 0; mi < MR; ++mi)
+            if (mi < nc)
+              v0[j * MR + mi] += blocks_dot_f32(w, s0, s1, reinterpret_cast<const float*>(opw[mi][c]));
+          // one row's widened codes live at a time
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
 #pragma unroll
@@ -321,6 +368,7 @@ struct Gemv {
         v0[j * MR + mi] = acc0;
         v1[j * MR + mi] = acc1;
       }
+    }
     }
     XRed<LPR / 2, NV>::run(v0, lane);
     if (GATEUP) XRed<LPR / 2, NV>::run(v1, lane);
@@ -434,6 +482,241 @@ struct Gemv {
   }
 };
 
+// Streaming GEMV (gate/up) for steps of two to four rows.  The weights stream
+// as in the one-row kernel (a lane owns 32 K-elements per 2048-wide chunk; the
+// next row step's loads are in flight while the current one is summed), each
+// chunk's codes are widened once, and every pick of the expert is computed
+// from them.  A cached step of M rows gives an expert at most M picks (a row's
+// top-k experts are distinct), so the operand rows (x or h) of an expert's at
+// most kSharedPicks picks sit in LDS, loaded once per block task and shared by
+// the block's four wavefronts: a block task is a run of one expert's row
+// steps, split among the wavefronts.  A row's products, its block-scale
+// products and its cross-lane sums are those of the one-row kernel, in the
+// same order, so each row's bits do not depend on how many rows the step has.
+// In LDS, operand piece v (16 bytes) of lane `seg` in a chunk sits in slot
+// v ^ sw(seg) of the lane's run, so eight neighbouring lanes reading their
+// v-th pieces hit eight different bank groups.
+constexpr int kSharedPicks = 4;
+
+template <int K, int R, bool GATEUP>
+struct GemvShared {
+  using G = Geo<K>;
+  static constexpr int NSEG = G::NSEG, LPR = G::LPR, RPW = G::RPW;
+  static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int MRX = kSharedPicks;
+  static constexpr int EB = GATEUP ? 2 : 4;             // operand bytes per element
+  static constexpr int ROWB = K * EB;                   // operand bytes per pick
+  static constexpr int PPL = 32 * EB / 16;              // 16-byte pieces per lane and chunk
+  static constexpr int NV = R * MRX;
+  static constexpr int LDS_B = MRX * ROWB;
+  static_assert(NV <= LPR, "too many values for the row group");
+
+  using Buf = typename Gemv<K, 1, R, GATEUP>::Buf;
+
+  __device__ static __forceinline__ int sw(int seg) { return EB == 2 ? ((seg >> 1) & 3) : (seg & 7); }
+  // byte offset of piece v of lane seg, chunk c, pick slot m
+  __device__ static __forceinline__ int lpos(int m, int c, int seg, int v) {
+    return m * ROWB + c * (2048 * EB) + seg * (PPL * 16) + 16 * (v ^ sw(seg));
+  }
+
+  // the operand rows of picks c0 .. c0 + nc - 1 into LDS (all threads of the block)
+  __device__ static __forceinline__ void stage_operand(const GemvArgs& a, uint8_t* lds, int c0, int nc) {
+    constexpr int PPR_ = ROWB / 16;                     // pieces per operand row
+    const int total = nc * PPR_;
+    for (int P = threadIdx.x; P < total; P += kGemvThreads) {
+      const int m = P / PPR_, q = P - m * PPR_;
+      const int p = a.uniq_picks[c0 + m];
+      const uint8_t* row = static_cast<const uint8_t*>(a.operand) +
+                           (GATEUP ? (size_t)(p / a.k) * K * 2 : (size_t)p * K * 4);
+      const int byte = 16 * q;
+      const int c = byte / (2048 * EB), rem = byte - c * (2048 * EB);
+      const int seg = rem / (PPL * 16), v = (rem / 16) % PPL;
+      *reinterpret_cast<uint4*>(lds + lpos(m, c, seg, v)) = ld16(row + byte);
+    }
+  }
+
+  // the lane's 32 operand elements of chunk c of pick slot m
+  __device__ static __forceinline__ void xread(const uint8_t* lds, int m, int c, int seg, uint32_t (&xv)[16 * EB / 2]) {
+#pragma unroll
+    for (int v = 0; v < PPL; ++v) {
+      const uint4 t = *reinterpret_cast<const uint4*>(lds + lpos(m, c, seg, v));
+      xv[4 * v + 0] = t.x;
+      xv[4 * v + 1] = t.y;
+      xv[4 * v + 2] = t.z;
+      xv[4 * v + 3] = t.w;
+    }
+  }
+
+  // seg_dot_bf16 with the codes already widened: w[4 * dw + sel] from dword dw
+  __device__ static __forceinline__ float blocks_dot(const bf16x2 (&w)[16], float s0, float s1, const uint32_t* xv) {
+    float bsum[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(w[blk * 8 + e], __builtin_bit_cast(bf16x2, xv[blk * 8 + e]), acc, false);
+      bsum[blk] = acc;
+    }
+    return fmaf(bsum[1], s1, bsum[0] * s0);
+  }
+
+  __device__ static __forceinline__ void process(const Buf& b, const uint8_t* lds, const int (&pk)[MRX], int nc, int i,
+                                                 int n, int base, int lane, int rsub, float gs, const GemvArgs& a) {
+    const int seg = lane % LPR;
+    float v0[NV], v1[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      v0[e] = 0.0f;
+      v1[e] = 0.0f;
+    }
+    if constexpr (GATEUP) {
+      // each chunk's codes are widened once, then used by every pick
+#pragma unroll
+      for (int c = 0; c < NSEG; ++c) {
+        bf16x2 wg[R][16], wu[R][16];
+        float sg[R][2], su[R][2];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const uint32_t dg[4] = {b.q[j][0][c].x, b.q[j][0][c].y, b.q[j][0][c].z, b.q[j][0][c].w};
+          const uint32_t du[4] = {b.q[j][1][c].x, b.q[j][1][c].y, b.q[j][1][c].z, b.q[j][1][c].w};
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            bf16x2 t[4];
+            fp4x8_bf16(dg[dw], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wg[j][4 * dw + e] = t[e];
+            fp4x8_bf16(du[dw], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wu[j][4 * dw + e] = t[e];
+          }
+          sg[j][0] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
+          sg[j][1] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
+          su[j][0] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][1][c], 0);
+          su[j][1] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][1][c], 1);
+        }
+#pragma unroll
+        for (int m = 0; m < MRX; ++m) {
+          if (m < nc) {
+            uint32_t xv[16];
+            xread(lds, m, c, seg, xv);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+              v0[j * MRX + m] += blocks_dot(wg[j], sg[j][0], sg[j][1], xv);
+              v1[j * MRX + m] += blocks_dot(wu[j], su[j][0], su[j][1], xv);
+            }
+          }
+        }
+      }
+    } else {
+      // one pick at a time: its operand slice serves the R rows, whose codes
+      // are widened again for each pick
+#pragma nounroll
+      for (int m = 0; m < nc; ++m) {
+        float acc[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[j] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NSEG; ++c) {
+          uint32_t xv[32];
+          xread(lds, m, c, seg, xv);
+#pragma unroll
+          for (int j = 0; j < R; ++j) {
+            // widened anew for each pick: keeping R rows widened across the
+            // picks would take 32 R registers
+            uint4 q = b.q[j][0][c];
+            asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+            acc[j] += seg_dot_f32(q, b.sc[j][0][c], reinterpret_cast<const float*>(xv));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int mm = 0; mm < MRX; ++mm)
+            if (mm == m) v0[j * MRX + mm] = acc[j];
+      }
+    }
+    XRed<LPR / 2, NV>::run(v0, lane);
+    if (GATEUP) XRed<LPR / 2, NV>::run(v1, lane);
+    const int g = lane % LPR;
+    if (g % (LPR / NV) == 0) {
+      const int idx = g / (LPR / NV);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int m = 0; m < MRX; ++m) {
+          if (idx == j * MRX + m && m < nc && i + j < n) {
+            const int r = (base + i + j) * RPW + rsub;
+            if (GATEUP)
+              store_h(a.out + (size_t)pk[m] * a.rows, r, silu_f32(v0[0] * gs) * (v1[0] * gs), a.split_h);
+            else
+              a.out[(size_t)pk[m] * a.rows + r] = v0[0] * gs;
+          }
+        }
+      }
+    }
+  }
+
+  __device__ static __forceinline__ void run(const GemvArgs& a, uint8_t* lds) {
+    const int U = a.hdr[H_UNIQUE];
+    if (U <= 0) return;
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int seg = lane % LPR, rsub = lane / LPR;
+    const int spu = a.rows / RPW;                 // row steps per expert
+    int tpe = (int)gridDim.x / U;                 // block tasks per expert
+    if (tpe < 1) tpe = 1;
+    if (tpe > spu) tpe = spu;
+    const int ntask = U * tpe;
+    int prev_u = -1;
+    for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
+      const int u = task / tpe, sub = task - u * tpe;
+      // the task's row steps [t0, t1), then the wavefront's share [base, base + n)
+      const int t0 = (int)((long)spu * sub / tpe), t1 = (int)((long)spu * (sub + 1) / tpe);
+      const int per = (t1 - t0 + 3) / 4;
+      const int base = t0 + w * per;
+      int n = t1 - base;
+      n = n < 0 ? 0 : n > per ? per : n;
+      const uint8_t* blob = a.uniq_ptr[u];
+      const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
+      const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
+      const int nc = off1 - off0 < MRX ? off1 - off0 : MRX;     // at most MRX on the steps this kernel serves
+      const uint8_t* code_base = blob + a.code_off + seg * 16;
+      const uint8_t* scale_base = blob + a.scale_off + seg * 2;
+      Buf A, B;
+      if (n > 0) Gemv<K, 1, R, GATEUP>::load(A, code_base, scale_base, 0, n, base, 1, rsub, a.up_row0);
+      if (u != prev_u) {
+        __syncthreads();                          // the block is done with the previous operands
+        stage_operand(a, lds, off0, nc);
+        __syncthreads();
+        prev_u = u;
+      }
+      int pk[MRX];
+#pragma unroll
+      for (int m = 0; m < MRX; ++m) pk[m] = m < nc ? a.uniq_picks[off0 + m] : 0;
+      if (n <= 0) continue;
+      int i = 0;
+      while (true) {
+        if (i + R < n) Gemv<K, 1, R, GATEUP>::load(B, code_base, scale_base, i + R, n, base, 1, rsub, a.up_row0);
+        process(A, lds, pk, nc, i, n, base, lane, rsub, gs, a);
+        i += R;
+        if (i >= n) break;
+        if (i + R < n) Gemv<K, 1, R, GATEUP>::load(A, code_base, scale_base, i + R, n, base, 1, rsub, a.up_row0);
+        process(B, lds, pk, nc, i, n, base, lane, rsub, gs, a);
+        i += R;
+        if (i >= n) break;
+      }
+    }
+  }
+};
+
+template <int K, int R, bool GATEUP>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv_shared(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GemvShared<K, R, GATEUP>::LDS_B];
+  span_start(a.span);
+  GemvShared<K, R, GATEUP>::run(a, lds);
+  span_end(a.span);
+}
+
 template <int K, int MR, int R, bool GATEUP, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   span_start(a.span);
@@ -477,21 +760,277 @@ __device__ __forceinline__ bf16x8 bf16x8_from_words(const uint4& v) {
 // The weights are staged through LDS.  Loaded in the MFMA layout directly (16
 // rows x 64 bytes per instruction) they peaked at about 4.5 TB/s in a
 // pure-read test, against 6.8 TB/s for loads of whole cache lines.  A task is
-// 32 weight rows of one unique expert (gate/up: one 16-row tile of gate and
-// the matching tile of up; down: two 16-row tiles) against up to 16 of its
-// picks.  K is walked in stages of KC elements: the stage's 32 x KC/2 code
-// bytes are loaded row-contiguously (whole 128-byte lines per row) into
-// registers, written to the wavefront's LDS buffer and read back in the MFMA
-// lane layout while the next stage's loads are in flight.  In LDS, 16-byte
-// piece c of row j sits in slot c ^ (j mod PPR) of its row, so the 16 lanes of
-// one MFMA operand read (16 rows, one piece each) hit 16 different bank
-// groups.  The operand (x or h) slices come from global memory one K tile
-// ahead.  (Direct-to-LDS loads cannot be prefetched this way: the compiler
-// waits for all of them before any LDS read.)
+// 16 * RT weight rows of one unique expert (gate/up: RT 16-row tiles of gate
+// and the matching tiles of up) against NCP of its picks per pass.  K is walked
+// in stages of KC elements: the stage's weight rows are loaded
+// row-contiguously (whole 128-byte lines per row) into registers, together
+// with the stage's operand slices (x or h) of the NCP pick columns, written to
+// the wavefront's LDS buffer and read back in the MFMA lane layout while the
+// next stage's loads (TWO: the next two stages') are in flight, so the operand
+// waits no longer than the weights do.  In LDS, 16-byte piece c of weight row
+// j sits in slot c ^ (j mod PPR) of its row, and operand chunk o of column n
+// in slot o ^ (n mod 8) of its column, so the lanes of one read hit different
+// bank groups.  Columns past the pass's picks load the last pick's operand
+// (their loads coalesce with its own): the products of one column do not mix
+// with the others', and only the picks' columns are stored; MFMA columns
+// NCP..15 repeat columns 0..NCP-1.  (Direct-to-LDS loads cannot be prefetched
+// this way: the compiler waits for all of them before any LDS read.)
+template <int K, bool GATEUP, int RT, int KCW, int NCP, bool TWO>
+struct GemvMfmaL {
+  static constexpr int NM = GATEUP ? 2 : 1;
+  static constexpr int NROW = 16 * RT * NM;            // weight rows per task
+  static constexpr int KC = K < KCW ? K : KCW;         // K elements per stage
+  static constexpr int NS = K / KC;                    // stages
+  static constexpr int PPR = KC / 32;                  // 16-byte code pieces per row and stage
+  static constexpr int CPL = NROW * PPR / 64;          // code pieces per lane and stage
+  static constexpr int SPR = KC / 64;                  // scale dwords per row and stage
+  static constexpr int SPL = NROW * SPR / 64;          // scale dwords per lane and stage
+  static constexpr int CODE_B = NROW * KC / 2;
+  static constexpr int W_B = CODE_B + NROW * KC / 16;  // weight bytes per stage
+  static constexpr int EB = GATEUP ? 2 : 4;            // operand bytes per element (h: bf16 high + low)
+  static constexpr int OCH = KC * EB / 16;             // 16-byte operand chunks per column and stage
+  static constexpr int XPL = NCP * OCH / 64;           // operand chunks per lane and stage
+  static constexpr int TCH = 128 * EB / 64;            // operand chunks a lane reads per K tile
+  static constexpr int STAGE_B = W_B + NCP * OCH * 16;
+  static constexpr int NKT = KC / 128;                 // K tiles per stage
+  static_assert(K % KC == 0 && KC % 128 == 0 && CPL >= 1 && SPL >= 1 && XPL >= 1, "unsupported K");
+  static_assert(OCH % 8 == 0, "the operand swizzle permutes groups of 8 chunks");
+
+  struct Regs {
+    uint4 c[CPL];
+    uint32_t s[SPL];
+    uint4 x[XPL];
+  };
+
+  // global row of task row j (a ragged task re-reads its last tile)
+  __device__ static __forceinline__ size_t grow(const GemvArgs& a, int tile0, int nt, int j) {
+    const int rt = j / (16 * NM), m = (j / 16) % NM, n = j % 16;
+    const int tile = tile0 + (rt < nt ? rt : nt - 1);
+    return (size_t)(tile * 16 + n + m * a.up_row0);
+  }
+
+  // xsrc: the operand row of the lane's column (lane mod 16); the lane loads
+  // its chunks lane / 16 + 4 i of the stage
+  __device__ static __forceinline__ void gload(Regs& r, const GemvArgs& a, const uint8_t* blob, const uint8_t* xsrc,
+                                               int tile0, int nt, int stage, int lane) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int L = 64 * i + lane, j = L / PPR, slot = L % PPR;
+      const int c = slot ^ (j % PPR);
+      r.c[i] = ld16_stream(blob + a.code_off + grow(a, tile0, nt, j) * (K / 2) + stage * (KC / 2) + 16 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int D = 64 * i + lane, j = D / SPR, dw = D % SPR;
+      r.s[i] = *(const __attribute__((address_space(1))) uint32_t*)(blob + a.scale_off + grow(a, tile0, nt, j) * (K / 16) +
+                                                                   stage * (KC / 16) + 4 * dw);
+    }
+    const uint8_t* xs = xsrc + (size_t)stage * (KC * EB) + 16 * (lane / NCP);
+#pragma unroll
+    for (int i = 0; i < XPL; ++i) r.x[i] = ld16(xs + (64 / NCP) * 16 * i);
+  }
+
+  __device__ static __forceinline__ void lstore(const Regs& r, uint8_t* buf, int lane) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int L = 64 * i + lane, j = L / PPR, slot = L % PPR;
+      *reinterpret_cast<uint4*>(buf + j * (KC / 2) + 16 * slot) = r.c[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int D = 64 * i + lane, j = D / SPR, dw = D % SPR;
+      *reinterpret_cast<uint32_t*>(buf + CODE_B + j * (KC / 16) + 4 * dw) = r.s[i];
+    }
+    const int n = lane % NCP;
+#pragma unroll
+    for (int i = 0; i < XPL; ++i) {
+      const int o = lane / NCP + (64 / NCP) * i;
+      *reinterpret_cast<uint4*>(buf + W_B + (n * OCH + (o ^ (n & 7))) * 16) = r.x[i];
+    }
+  }
+
+  // the products of K tile kt' of the stage in buf
+  __device__ static __forceinline__ void tile(const uint8_t* buf, int ktp, f32x4 (&acc)[RT][NM], int g, int n) {
+    uint4 x[TCH];
+    const int nn = n % NCP;    // columns NCP.. repeat the first ones; their products are not stored
+#pragma unroll
+    for (int v = 0; v < TCH; ++v) {
+      const int o = TCH * (4 * ktp + g) + v;
+      x[v] = *reinterpret_cast<const uint4*>(buf + W_B + (nn * OCH + (o ^ (nn & 7))) * 16);
+    }
+    bf16x8 bh[4], bl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (GATEUP) {
+        bh[q] = bf16x8_from_words(x[q]);
+      } else {
+        // h arrives split (store_h): 8 high parts, then their 8 low parts
+        bh[q] = bf16x8_from_words(x[2 * q]);
+        bl[q] = bf16x8_from_words(x[2 * q + 1]);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int j = (rt * NM + m) * 16 + n;
+        const int slot = (4 * ktp + g) ^ (j % PPR);
+        const uint4 q4 = *reinterpret_cast<const uint4*>(buf + j * (KC / 2) + 16 * slot);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(buf + CODE_B + j * (KC / 16) + 8 * ktp + 2 * g);
+        const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+        const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
+        const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 av = fp4x8_scaled_bf16(d[q], q < 2 ? s0 : s1);
+          acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[q], acc[rt][m], 0, 0, 0);
+          if (!GATEUP) acc[rt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[q], acc[rt][m], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // LDS writes of this wavefront are complete and ordered before its later reads
+  __device__ static __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // One LDS buffer per wavefront: a stage's writes follow the reads of the
+  // stage before in the wavefront's own program order, and the LDS serves a
+  // wavefront's accesses in that order.
+  __device__ static __forceinline__ void run(const GemvArgs& a, uint8_t* lds) {
+    int lo, U;
+    launch_uniques(a, a.hdr[H_UNIQUE], lo, U);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int nwaves = gridDim.x * (kGemvThreads / 64);
+    const int w = wave_id();
+    const int gw = blockIdx.x * (kGemvThreads / 64) + w;
+    uint8_t* buf = lds + (size_t)w * STAGE_B;
+    const int ntiles = a.rows / 16;
+    const int tpu = (ntiles + RT - 1) / RT;     // tasks per unique expert
+    const int ntask = U * tpu;
+    for (int task = gw; task < ntask; task += nwaves) {
+      const int u = unique_at(a, lo, task / tpu), tg = task - (task / tpu) * tpu;
+      const int tile0 = tg * RT;
+      const int nt = ntiles - tile0 < RT ? ntiles - tile0 : RT;
+      const uint8_t* blob = a.uniq_ptr[u];
+      const float gs = a.gs[2 * a.uniq_expert[u] + (GATEUP ? 0 : 1)];
+      const int off0 = a.uniq_off[u], off1 = a.uniq_off[u + 1];
+      for (int c0 = off0; c0 < off1; c0 += NCP) {
+        const int nc = off1 - c0 < NCP ? off1 - c0 : NCP;
+        const bool live = n < nc;
+        const int p = a.uniq_picks[c0 + (live ? n : nc - 1)];
+        const int ln = lane % NCP;    // the column whose operand this lane loads
+        const int pl = a.uniq_picks[c0 + (ln < nc ? ln : nc - 1)];
+        const uint8_t* xsrc = static_cast<const uint8_t*>(a.operand) +
+                              (GATEUP ? (size_t)(pl / a.k) * K * 2 : (size_t)pl * K * 4);
+        f32x4 acc[RT][NM];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (TWO) {
+        // two register stages in flight: RA and RB hold stages st + 1 and st + 2.
+        // The steady-state loop issues its loads unconditionally (a skipped
+        // load on one path makes the compiler wait for every load on both).
+        Regs RA, RB;
+        gload(RA, a, blob, xsrc, tile0, nt, 0, lane);
+        lstore(RA, buf, lane);
+        if (NS > 1) gload(RA, a, blob, xsrc, tile0, nt, 1, lane);
+        if (NS > 2) gload(RB, a, blob, xsrc, tile0, nt, 2, lane);
+        lds_sync();
+        int st = 0;
+        for (; st + 4 < NS; st += 2) {
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) tile(buf, ktp, acc, g, n);
+          lstore(RA, buf, lane);
+          gload(RA, a, blob, xsrc, tile0, nt, st + 3, lane);
+          lds_sync();
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) tile(buf, ktp, acc, g, n);
+          lstore(RB, buf, lane);
+          gload(RB, a, blob, xsrc, tile0, nt, st + 4, lane);
+          lds_sync();
+        }
+        // the last stages (at most four)
+        while (true) {
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) tile(buf, ktp, acc, g, n);
+          if (st + 1 >= NS) break;
+          lstore(RA, buf, lane);
+          if (st + 3 < NS) gload(RA, a, blob, xsrc, tile0, nt, st + 3, lane);
+          lds_sync();
+          ++st;
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) tile(buf, ktp, acc, g, n);
+          if (st + 1 >= NS) break;
+          lstore(RB, buf, lane);
+          if (st + 3 < NS) gload(RB, a, blob, xsrc, tile0, nt, st + 3, lane);
+          lds_sync();
+          ++st;
+        }
+        } else {
+        Regs R;
+        gload(R, a, blob, xsrc, tile0, nt, 0, lane);
+        lstore(R, buf, lane);
+        if (NS > 1) gload(R, a, blob, xsrc, tile0, nt, 1, lane);
+        lds_sync();
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+          for (int ktp = 0; ktp < NKT; ++ktp) tile(buf, ktp, acc, g, n);
+          if (st + 1 < NS) {
+            lstore(R, buf, lane);
+            if (st + 2 < NS) gload(R, a, blob, xsrc, tile0, nt, st + 2, lane);
+            lds_sync();
+          }
+        }
+        }
+        if (live) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            if (rt >= nt) break;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              v[j] = GATEUP ? silu_f32(acc[rt][0][j] * gs) * (acc[rt][NM - 1][j] * gs) : acc[rt][0][j] * gs;
+            const int r0 = (tile0 + rt) * 16 + 4 * g;      // r0 % 8 is 0 or 4
+            float* row = a.out + (size_t)p * a.rows;
+            if (GATEUP && a.split_h) {
+              bf16x4 hi4, lo4;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                __bf16 h, l;
+                split_bf16(v[j], h, l);
+                hi4[j] = h;
+                lo4[j] = l;
+              }
+              __bf16* grp = reinterpret_cast<__bf16*>(row) + (r0 / 8) * 16 + (r0 % 8);
+              *reinterpret_cast<bf16x4*>(grp) = hi4;
+              *reinterpret_cast<bf16x4*>(grp + 8) = lo4;
+            } else {
+              *reinterpret_cast<float4*>(row + r0) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+          }
+        }
+        // the next task's first stage overwrites the buffer this one has read
+        lds_sync();
+      }
+    }
+  }
+};
+
+// The matrix-core form for larger steps' down product: the weights are staged
+// through two LDS buffers per wavefront as above, and each lane reads its
+// pick column's operand slice from global memory one K tile ahead.  Tasks of
+// 64 rows against 16 columns read the operand once per 64 weight rows.
 constexpr int kLdsStageK = 256;
 
 template <int K, bool GATEUP, int RT>
-struct GemvMfmaL {
+struct GemvMfmaX {
   static constexpr int NM = GATEUP ? 2 : 1;
   static constexpr int NROW = 16 * RT * NM;            // weight rows per task
   static constexpr int KC = K < kLdsStageK ? K : kLdsStageK;   // K elements per stage
@@ -624,7 +1163,7 @@ struct GemvMfmaL {
       for (int c0 = off0; c0 < off1; c0 += 16) {
         const int nc = off1 - c0 < 16 ? off1 - c0 : 16;
         const bool live = n < nc;
-        const int p = live ? a.uniq_picks[c0 + n] : 0;
+        const int p = a.uniq_picks[c0 + (live ? n : nc - 1)];
         const uint8_t* xsrc = static_cast<const uint8_t*>(a.operand) +
                               (GATEUP ? (size_t)(p / a.k) * K * 2 : (size_t)p * K * 4);
         f32x4 acc[RT][NM];
@@ -698,26 +1237,35 @@ struct GemvMfmaL {
   }
 };
 
-// 16-row tiles per task: 32 weight rows for gate/up (a gate tile and its up
-// tile), 64 for down.  Each task reloads its picks' operand slices from L2
-// for every K tile, so larger tasks cut that traffic per weight byte; at 64
-// rows the down kernel holds about 270 registers (one wavefront per SIMD) and
-// is still faster than at 32 (GLM layer, M = 16: 91 against 105 us); 64-row
-// gate/up tasks gained nothing.
-constexpr int kMfmaTilesGateup = 1;
-constexpr int kMfmaTilesDown = 4;
-template <bool GATEUP>
-constexpr int mfma_tiles() { return GATEUP ? kMfmaTilesGateup : kMfmaTilesDown; }
 
-// LDS of the staged kernel: two stage buffers per wavefront.
-template <int K, bool GATEUP>
-constexpr int mfma_lds_bytes() { return (kGemvThreads / 64) * 2 * GemvMfmaL<K, GATEUP, mfma_tiles<GATEUP>()>::STAGE_B; }
+// Matrix-core task shapes, by the number NCP of pick columns a pass computes.
+// Steps of up to 8 rows (NCP = 8): gate/up tasks are one gate and one up tile
+// with two register stages in flight; down tasks are two tiles (32 rows) with
+// one.  Larger steps (NCP = 16; an expert has up to 16 picks on a cached step):
+// gate/up as above with one register stage; down tasks are four tiles (64
+// rows) whose operand comes from global memory one K tile ahead (GemvMfmaX),
+// which halves the operand traffic per weight byte.  All stages are 256 wide.
+// Each wavefront's LDS holds 8.5 to 18 KiB, so that two or three blocks of
+// four wavefronts fit a compute unit, as many as their registers allow.
+constexpr int kMfmaStage = 256;
+template <int K, bool GATEUP, int NCP>
+using MfmaTask = typename std::conditional<
+    GATEUP, GemvMfmaL<K, true, 1, kMfmaStage, NCP, NCP == 8>,
+    typename std::conditional<NCP == 8, GemvMfmaL<K, false, 2, kMfmaStage, 8, false>,
+                              GemvMfmaX<K, false, 4>>::type>::type;
+// 16-row tiles per task
+constexpr int mfma_tiles(bool gateup, int ncp) { return gateup ? 1 : ncp == 8 ? 2 : 4; }
 
-template <int K, bool GATEUP>
+template <int K, bool GATEUP, int NCP>
+constexpr int mfma_lds_bytes() {
+  return (kGemvThreads / 64) * (!GATEUP && NCP == 16 ? 2 : 1) * MfmaTask<K, GATEUP, NCP>::STAGE_B;
+}
+
+template <int K, bool GATEUP, int NCP>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv_mfma_lds(GemvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<K, GATEUP>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[mfma_lds_bytes<K, GATEUP, NCP>()];
   span_start(a.span);
-  GemvMfmaL<K, GATEUP, mfma_tiles<GATEUP>()>::run(a, lds);
+  MfmaTask<K, GATEUP, NCP>::run(a, lds);
   span_end(a.span);
 }
 
@@ -836,7 +1384,7 @@ typedef void (*GemvFn)(GemvArgs);
 template <int K, int MR, bool GATEUP>
 constexpr int stage_rows() {
   constexpr int lim = Geo<K>::LPR / MR;
-  constexpr int want = GATEUP ? 1 : 4;
+  constexpr int want = GATEUP ? 1 : MR > 2 ? 2 : 4;
   return want < lim ? want : lim;
 }
 
@@ -866,7 +1414,7 @@ GemvFn pick_gemv(int K) {
 int rows_per_wave(int K) { return K >= 2048 ? 1 : 2048 / K; }
 int stage_rows_rt(int K, int MR, bool gateup) {
   const int lpr = K >= 2048 ? 64 : K / 32;
-  const int want = gateup ? 1 : 4;
+  const int want = gateup ? 1 : MR > 2 ? 2 : 4;
   return want < lpr / MR ? want : lpr / MR;
 }
 
@@ -902,20 +1450,25 @@ int mr_for(int M) { return M == 1 ? 1 : 2; }
 constexpr int kMfmaMinRowsGateup = SC_MFMA_MIN_ROWS_GATEUP;
 constexpr int kMfmaMinRowsDown = SC_MFMA_MIN_ROWS_DOWN;
 
-template <bool GATEUP>
-GemvFn pick_mfma(int K) {
+template <bool GATEUP, int NCP>
+GemvFn pick_mfma_n(int K) {
   switch (K) {
-    case 128: return GATEUP ? nullptr : k_gemv_mfma_lds<128, GATEUP>;
-    case 256: return k_gemv_mfma_lds<256, GATEUP>;
-    case 512: return k_gemv_mfma_lds<512, GATEUP>;
-    case 1024: return k_gemv_mfma_lds<1024, GATEUP>;
-    case 2048: return k_gemv_mfma_lds<2048, GATEUP>;
-    case 4096: return k_gemv_mfma_lds<4096, GATEUP>;
-    case 6144: return k_gemv_mfma_lds<6144, GATEUP>;
-    case 8192: return k_gemv_mfma_lds<8192, GATEUP>;
+    case 128: return GATEUP ? nullptr : k_gemv_mfma_lds<128, GATEUP, NCP>;
+    case 256: return k_gemv_mfma_lds<256, GATEUP, NCP>;
+    case 512: return k_gemv_mfma_lds<512, GATEUP, NCP>;
+    case 1024: return k_gemv_mfma_lds<1024, GATEUP, NCP>;
+    case 2048: return k_gemv_mfma_lds<2048, GATEUP, NCP>;
+    case 4096: return k_gemv_mfma_lds<4096, GATEUP, NCP>;
+    case 6144: return k_gemv_mfma_lds<6144, GATEUP, NCP>;
+    case 8192: return k_gemv_mfma_lds<8192, GATEUP, NCP>;
     default: return nullptr;
   }
 }
+// Pick columns per matrix-core pass for a step of M rows (a cached step gives
+// an expert at most M picks).
+int mfma_columns(int M) { return M <= 8 ? 8 : 16; }
+template <bool GATEUP>
+GemvFn pick_mfma(int K, int ncp) { return ncp == 8 ? pick_mfma_n<GATEUP, 8>(K) : pick_mfma_n<GATEUP, 16>(K); }
 
 // One wavefront per task (RT 16-row tiles of one expert), at most cap blocks.
 constexpr int kMfmaBlocksGateup = 768;
@@ -927,6 +1480,38 @@ int mfma_blocks(long maxu, int rows, int rt, int cap) {
   if (blocks > cap) blocks = cap;
   return (int)blocks;
 }
+
+// Shared-operand streaming kernels (steps of 2 .. kSharedPicks rows): row
+// steps per pipeline stage as the one-row kernels take them, within what the
+// row group can reduce for kSharedPicks picks; null where the operand rows of
+// kSharedPicks picks would not fit 64 KiB of LDS.
+template <int K, bool GATEUP>
+constexpr int shared_rows() {
+  constexpr int lim = Geo<K>::LPR / kSharedPicks;
+  constexpr int want = GATEUP ? 1 : 4;
+  return want < lim ? want : lim;
+}
+template <int K, bool GATEUP>
+GemvFn shared_fn() {
+  if constexpr (GemvShared<K, shared_rows<K, GATEUP>(), GATEUP>::LDS_B > 65536) return nullptr;
+  else return k_gemv_shared<K, shared_rows<K, GATEUP>(), GATEUP>;
+}
+template <bool GATEUP>
+GemvFn pick_shared(int K) {
+  switch (K) {
+    case 128: return GATEUP ? nullptr : shared_fn<128, GATEUP>();
+    case 256: return shared_fn<256, GATEUP>();
+    case 512: return shared_fn<512, GATEUP>();
+    case 1024: return shared_fn<1024, GATEUP>();
+    case 2048: return shared_fn<2048, GATEUP>();
+    case 4096: return shared_fn<4096, GATEUP>();
+    case 6144: return shared_fn<6144, GATEUP>();
+    case 8192: return shared_fn<8192, GATEUP>();
+    default: return nullptr;
+  }
+}
+// A cached step of 2 .. kSharedPicks rows gives each expert at most M picks.
+bool shared_step(int M, int group) { return M >= 2 && M <= kSharedPicks && group < 0; }
 
 }  // namespace
 
@@ -973,10 +1558,16 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   GemvArgs a = gateup_args(sh, W, gs, x, group);
   a.split_h = mfma && M >= kMfmaMinRowsDown;   // the down product of this step runs on the matrix cores
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
+  if (shared_step(M, group) && pick_shared<true>(sh.H)) {
+    const int blocks = gemv_blocks(maxu * (sh.I / rows_per_wave(sh.H)), kGateupBlocks);
+    a.span = ev.span_for(blocks);
+    return sc_launch(pick_shared<true>(sh.H), dim3(blocks), dim3(kGemvThreads), st, ev, a);
+  }
   if (mfma && M >= kMfmaMinRowsGateup) {
-    GemvFn fn = pick_mfma<true>(sh.H);
+    const int ncp = mfma_columns(M);
+    GemvFn fn = pick_mfma<true>(sh.H, ncp);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.I, kMfmaTilesGateup, kMfmaBlocksGateup);
+    const int blocks = mfma_blocks(maxu, sh.I, mfma_tiles(true, ncp), kMfmaBlocksGateup);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
@@ -1059,11 +1650,17 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
   a.scale_off = sh.off_w2s;
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (mfma && M >= kMfmaMinRowsDown) {
-    GemvFn fn = pick_mfma<false>(sh.I);
+    const int ncp = mfma_columns(M);
+    GemvFn fn = pick_mfma<false>(sh.I, ncp);
     if (!fn) return hipErrorInvalidValue;
-    const int blocks = mfma_blocks(maxu, sh.H, kMfmaTilesDown, kMfmaBlocksDown);
+    const int blocks = mfma_blocks(maxu, sh.H, mfma_tiles(false, ncp), kMfmaBlocksDown);
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
+  }
+  if (shared_step(M, group) && pick_gemv<false, 4>(sh.I)) {
+    const int blocks = gemv_blocks(maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, 4, false), kDownBlocks);
+    a.span = ev.span_for(blocks);
+    return sc_launch(pick_gemv<false, 4>(sh.I), dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
   const int mr = mr_for(M);
   GemvFn fn = M == 1 ? pick_gemv<false, 0>(sh.I) : pick_gemv<false, 2>(sh.I);

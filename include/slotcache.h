@@ -131,8 +131,11 @@ typedef struct {
 /* Without SC_FLAG_BATCH_INVARIANT, steps of at least this many rows run the
  * gate/up (resp. down) product on the matrix cores; their rows need not be
  * bit-equal to the same rows decoded alone (the outputs stay within the same
- * tolerance of the exact result). */
-#define SC_MFMA_MIN_ROWS_GATEUP 3
+ * tolerance of the exact result).  Below them the streaming kernels run, whose
+ * rows are bit-equal to one-row steps: on steps of 2 to 4 rows the gate/up
+ * kernel keeps the expert's pick operands in LDS and widens each weight once
+ * for all of them. */
+#define SC_MFMA_MIN_ROWS_GATEUP 5
 #define SC_MFMA_MIN_ROWS_DOWN 3
 
 typedef struct {
