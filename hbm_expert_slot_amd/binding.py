@@ -21,7 +21,7 @@ SC_BYPASS_ROWS = 16
 SC_FLAG_BATCH_INVARIANT = 1
 SC_FLAG_OVERLAP_FILL = 2
 SC_MFMA_MIN_ROWS_GATEUP = 5
-SC_MFMA_MIN_ROWS_DOWN = 3
+SC_MFMA_MIN_ROWS_DOWN = 5
 SC_N_KERNELS = 5
 SC_N_EVENTS = 2 * SC_N_KERNELS
 SC_STATIC_SCRATCH_BYTES = 16777216

@@ -482,11 +482,11 @@ struct Gemv {
   }
 };
 
-// Streaming GEMV (gate/up) for steps of two to four rows.  The weights stream
-// as in the one-row kernel (a lane owns 32 K-elements per 2048-wide chunk; the
-// next row step's loads are in flight while the current one is summed), each
-// chunk's codes are widened once, and every pick of the expert is computed
-// from them.  A cached step of M rows gives an expert at most M picks (a row's
+// Streaming GEMVs for steps of two to four rows.  The weights stream as in
+// the one-row kernels (a lane owns 32 K-elements per 2048-wide chunk; the next
+// row steps' loads are in flight while the current ones are summed), each
+// chunk's codes are widened once (gate/up to bf16 pairs, down to fp32), and
+// every pick of the expert is computed from them.  A cached step of M rows gives an expert at most M picks (a row's
 // top-k experts are distinct), so the operand rows (x or h) of an expert's at
 // most kSharedPicks picks sit in LDS, loaded once per block task and shared by
 // the block's four wavefronts: a block task is a run of one expert's row
@@ -609,31 +609,36 @@ struct GemvShared {
         }
       }
     } else {
-      // one pick at a time: its operand slice serves the R rows, whose codes
-      // are widened again for each pick
-#pragma nounroll
-      for (int m = 0; m < nc; ++m) {
-        float acc[R];
+      // the stage's R rows are widened to fp32 once per chunk; each pick's
+      // operand slice is read from LDS once per chunk and serves the R rows
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[j] = 0.0f;
+      for (int c = 0; c < NSEG; ++c) {
+        f32x2 w[R][16];
+        float s0[R], s1[R];
 #pragma unroll
-        for (int c = 0; c < NSEG; ++c) {
-          uint32_t xv[32];
-          xread(lds, m, c, seg, xv);
+        for (int j = 0; j < R; ++j) {
+          const uint32_t d[4] = {b.q[j][0][c].x, b.q[j][0][c].y, b.q[j][0][c].z, b.q[j][0][c].w};
 #pragma unroll
-          for (int j = 0; j < R; ++j) {
-            // widened anew for each pick: keeping R rows widened across the
-            // picks would take 32 R registers
-            uint4 q = b.q[j][0][c];
-            asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-            acc[j] += seg_dot_f32(q, b.sc[j][0][c], reinterpret_cast<const float*>(xv));
+          for (int dw = 0; dw < 4; ++dw) {
+            f32x2 t[4];
+            fp4x8_f32(d[dw], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[j][4 * dw + e] = t[e];
           }
+          s0[j] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
+          s1[j] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
         }
 #pragma unroll
-        for (int j = 0; j < R; ++j)
+        for (int m = 0; m < MRX; ++m) {
+          if (m < nc) {
+            uint32_t xv[32];
+            xread(lds, m, c, seg, xv);
 #pragma unroll
-          for (int mm = 0; mm < MRX; ++mm)
-            if (mm == m) v0[j * MRX + mm] = acc[j];
+            for (int j = 0; j < R; ++j)
+              v0[j * MRX + m] += Gemv<K, 1, R, false>::blocks_dot_f32(w[j], s0[j], s1[j],
+                                                                     reinterpret_cast<const float*>(xv));
+          }
+        }
       }
     }
     XRed<LPR / 2, NV>::run(v0, lane);
@@ -1439,6 +1444,10 @@ constexpr int kGateupBlocks = 768;
 constexpr int kFillBlocks = 512;
 constexpr int kFillBlocksShared = 256;
 constexpr int kDownBlocks = 512;
+// Shared-operand streaming kernels (steps of 2 to 4 rows): 146 to 153 VGPRs
+// and 32 to 48 KiB of LDS, three blocks per compute unit, so 768 blocks are
+// all resident (down at M = 4 with 512 blocks: 44.6 against 36.4 us).
+constexpr int kSharedBlocks = 768;
 
 int mr_for(int M) { return M == 1 ? 1 : 2; }
 
@@ -1488,7 +1497,7 @@ int mfma_blocks(long maxu, int rows, int rt, int cap) {
 template <int K, bool GATEUP>
 constexpr int shared_rows() {
   constexpr int lim = Geo<K>::LPR / kSharedPicks;
-  constexpr int want = GATEUP ? 1 : 4;
+  constexpr int want = GATEUP ? 1 : 2;
   return want < lim ? want : lim;
 }
 template <int K, bool GATEUP>
@@ -1559,7 +1568,7 @@ hipError_t launch_gateup(const Shape& sh, const Workspace& W, const float* gs, c
   a.split_h = mfma && M >= kMfmaMinRowsDown;   // the down product of this step runs on the matrix cores
   const long maxu = (long)(M * sh.k < sh.E ? M * sh.k : sh.E);
   if (shared_step(M, group) && pick_shared<true>(sh.H)) {
-    const int blocks = gemv_blocks(maxu * (sh.I / rows_per_wave(sh.H)), kGateupBlocks);
+    const int blocks = gemv_blocks(maxu * (sh.I / rows_per_wave(sh.H)), kSharedBlocks);
     a.span = ev.span_for(blocks);
     return sc_launch(pick_shared<true>(sh.H), dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
@@ -1657,10 +1666,18 @@ hipError_t launch_down(const Shape& sh, const Workspace& W, const float* gs, int
     a.span = ev.span_for(blocks);
     return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
   }
-  if (shared_step(M, group) && pick_gemv<false, 4>(sh.I)) {
-    const int blocks = gemv_blocks(maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, 4, false), kDownBlocks);
-    a.span = ev.span_for(blocks);
-    return sc_launch(pick_gemv<false, 4>(sh.I), dim3(blocks), dim3(kGemvThreads), st, ev, a);
+  if (shared_step(M, group)) {
+    if (GemvFn fn = pick_shared<false>(sh.I)) {
+      const int blocks = gemv_blocks(maxu * (sh.H / rows_per_wave(sh.I)), kSharedBlocks);
+      a.span = ev.span_for(blocks);
+      return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
+    }
+    if (GemvFn fn = pick_gemv<false, 4>(sh.I)) {
+      // operand rows too large for LDS: four picks' slices in registers
+      const int blocks = gemv_blocks(maxu * (sh.H / rows_per_wave(sh.I)) / stage_rows_rt(sh.I, 4, false), kDownBlocks);
+      a.span = ev.span_for(blocks);
+      return sc_launch(fn, dim3(blocks), dim3(kGemvThreads), st, ev, a);
+    }
   }
   const int mr = mr_for(M);
   GemvFn fn = M == 1 ? pick_gemv<false, 0>(sh.I) : pick_gemv<false, 2>(sh.I);

@@ -106,7 +106,7 @@ typedef struct {
  * order does not depend on how many rows share an expert) and the matrix-core
  * kernels, whose rounding differs, are not used.  Drafted and verify rows then
  * never change a row's output (the exact-decoding rule on the page "TensorFold
- * GLM-5.3 explained").  Costs speed from M = 3 on (the matrix-core ranges
+ * GLM-5.3 explained").  Costs speed from M = 5 on (the matrix-core ranges
  * below). */
 #define SC_FLAG_BATCH_INVARIANT 1u
 
@@ -132,11 +132,11 @@ typedef struct {
  * gate/up (resp. down) product on the matrix cores; their rows need not be
  * bit-equal to the same rows decoded alone (the outputs stay within the same
  * tolerance of the exact result).  Below them the streaming kernels run, whose
- * rows are bit-equal to one-row steps: on steps of 2 to 4 rows the gate/up
- * kernel keeps the expert's pick operands in LDS and widens each weight once
- * for all of them. */
+ * rows are bit-equal to one-row steps: on steps of 2 to 4 rows both products
+ * keep the expert's pick operands in LDS and widen each weight once for all
+ * of them. */
 #define SC_MFMA_MIN_ROWS_GATEUP 5
-#define SC_MFMA_MIN_ROWS_DOWN 3
+#define SC_MFMA_MIN_ROWS_DOWN 5
 
 typedef struct {
   size_t blob_bytes;              /* B_e */
