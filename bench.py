@@ -80,9 +80,15 @@ def parse():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/pmc_gateup_glm_m1.json and pmc_down_glm_m1.json from the rocprofv3 "
                          "--pmc counter files of a bench run and of the --calibrate-copy run")
-    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "STEPS_JSON"),
+    ap.add_argument("--trace-summary", nargs=3, metavar=("KERNEL_TRACE_CSV", "KERNEL_STATS_CSV", "STEPS_JSON"),
                     help="only summarize a rocprofv3 kernel trace of this bench: each kernel's duration over "
-                         "the all-hit block's timed launches listed by --dump-steps")
+                         "the all-hit block's timed launches listed by --dump-steps (written to "
+                         "profiles/dur_allhit_glm_m1.json), and the run's kernel statistics (written to "
+                         "profiles/glm_m1_decode_step_kernels.md)")
+    ap.add_argument("--sweep-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "SWEEP_OUTPUT"),
+                    help="only summarize a rocprofv3 kernel trace of a --sweep-rows run (its JSON lines in "
+                         "SWEEP_OUTPUT): each kernel's duration per M, written to "
+                         "profiles/glm_drafted_rows_kernels.md")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (counter calibration)")
     a = ap.parse_args()
@@ -749,6 +755,7 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     from synth import CONFIGS
     gb, db = gemv_bytes(CONFIGS["glm"])
     src = source_hash()
+    table = []
     for key, name, algo in (("gateup_glm_m1", KERNEL_NAMES["gateup"], gb), ("down_glm_m1", KERNEL_NAMES["down"], db)):
         f, full = per_dispatch(fetch_csv, "FETCH_SIZE", name)
         w, _ = per_dispatch(write_csv, "WRITE_SIZE", name)
@@ -768,6 +775,19 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
         with open(os.path.join(ROOT, "profiles", "pmc_%s.json" % key), "w") as fh:
             json.dump(out, fh, indent=1)
         print(key, out["kernel"], "bytes/launch", bpl, "ratio", round(bpl / algo, 4), "dispatches", len(f))
+        table.append("| `%s` | %.1f | %.1f | %d | %d | %.4f |" % (kernel_label(full), fm, wm, bpl, algo, bpl / algo))
+    L = ["# HBM traffic of the FP4 GEMV kernels (rocprofv3 counters), GLM layer M=1\n",
+         "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, TCC) were taken in separate runs, then scaled by what the same "
+         "counters read for a plain 1 GiB device copy (torch `copy_`, kernel `__amd_rocclr_copyBuffer`): FETCH_SIZE "
+         "reads %.4f of the bytes read, WRITE_SIZE %.4f of the bytes written.  Medians over each kernel's one-row "
+         "dispatches (%d per kernel) of a `bench.py --steps 20 --warmup 4` run.\n" % (ff, wf, len(f)),
+         "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) | algorithmic bytes | ratio |",
+         "|---|---|---|---|---|---|"] + table + [
+         "", "`bench.py` reports these bytes as `roofline.traffic` while the GEMV source hash recorded in "
+         "`pmc_gateup_glm_m1.json` / `pmc_down_glm_m1.json` matches.\n",
+         "Commands (`$REPO` = repository root on the GPU host):\n", "```"] + PMC_COMMANDS + ["```"]
+    with open(os.path.join(ROOT, "profiles", "pmc_gemv_glm_m1.md"), "w") as fh:
+        fh.write("\n".join(L) + "\n")
 
 
 def prefill(a, torch, SlotCache, CONFIGS, activations, expert_blobs, global_scales, routing_trace):
@@ -877,7 +897,144 @@ def drafted_workload(torch, SlotCache, CONFIGS, activations, expert_blobs, globa
             "timing": "one HIP-graph replay of the steps (each after the cache sweep) minus a replay of the sweeps alone"}
 
 
-def trace_summary(trace_csv, steps_json):
+def kernel_label(name):
+    """A rocprofv3 kernel name without the anonymous-namespace qualifier and the argument list."""
+    n = name.replace("(anonymous namespace)::", "").split("(")[0].strip()
+    if "reduce_kernel" in n:
+        return "at::native::reduce_kernel (the read sweep between steps)"
+    if "rocclr_copyBuffer" in n:
+        return "__amd_rocclr_copyBuffer (bench plumbing: inputs, state restore)"
+    if "rocclr_fillBuffer" in n:
+        return "__amd_rocclr_fillBufferAligned (bench plumbing)"
+    if "elementwise" in n:
+        return "at::native elementwise (setup)"
+    return n.replace("void ", "")
+
+
+def trace_markdown(stats_csv, dur):
+    """profiles/glm_m1_decode_step_kernels.md: the run's per-kernel statistics and the all-hit
+    block's timed launches by rocprofv3, the kernels' own spans and their event pairs."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    L = ["# Kernel durations: GLM-shaped MoE layer decode step, M=1 (rocprofv3 kernel trace)\n",
+         "Workload: H 6144, I 2048, 256 experts, top-8, NVFP4, Zipf(1.1)-skewed routing.  One `bench.py` process: "
+         "first the all-hit block (every expert resident, %d untimed + %d timed one-row steps, each after a "
+         "512 MiB read sweep, then graph replays), then the churning 128-slot layer (32 cache warm-up + 5 warmup + "
+         "20 timed eager steps, then graph replays of the 20 steps from the restored state), then the drafted-rows "
+         "workload (M = 4 / 16 / 64).\n" % (dur["all_hit_warm"], dur["timed_launches"]),
+         "Commands (`$REPO` = repository root on the GPU host):\n", "```"] + dur["commands"] + ["```\n",
+         "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:16]:
+        L.append("| `%s` | %s | %.2f | %.2f | %.2f | %.2f |" % (kernel_label(r["Name"]), r["Calls"],
+                 float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                 float(r["TotalDurationNs"]) / 1e6))
+    L += ["", "## The all-hit block's timed launches (the roofline kernels)\n",
+          "Each kernel of the one-row step over the %d timed all-hit launches (the block's launches come first in "
+          "the process, so launch `%d + j` of each kernel is timed step `j`):\n" % (dur["timed_launches"],
+                                                                                    dur["all_hit_warm"]),
+          "| kernel | rocprofv3 dispatch avg us | own device-clock spans avg us | hipExtLaunchKernelGGL event pair avg us |",
+          "|---|---|---|---|"]
+    for p in ("route_remap", "fill", "gateup", "down", "combine"):
+        L.append("| `%s` (%s) | %.3f | %.3f | %.3f |" % (dur["kernel_names"][p].rstrip("("), p,
+                 dur["rocprof_avg_us"][p], dur["spans_avg_us"][p], dur["events_avg_us"][p]))
+    gu, dn = gemv_bytes(CONFIGS_GLM())
+    g, d = dur["rocprof_avg_us"]["gateup"], dur["rocprof_avg_us"]["down"]
+    L += ["", "At the rocprofv3 durations: gate/up %d B / %.3f us = %.1f GB/s = %.4f of 8 TB/s; down %d B / %.3f us = "
+          "%.1f GB/s = %.4f; the pair %d B / %.3f us = %.4f (0.70 of peak is %.2f us for the pair)."
+          % (gu, g, gu / g / 1e3, gu / g / 1e3 / 8000, dn, d, dn / d / 1e3, dn / d / 1e3 / 8000, gu + dn, g + d,
+             (gu + dn) / (g + d) / 1e3 / 8000, (gu + dn) / (0.7 * 8e12) * 1e6),
+          "The dispatch window includes the wave launch before the first block starts and the end-of-kernel signal "
+          "after the last wavefront, which the kernels' own stamps do not; the event pairs' stop lands a few "
+          "microseconds after the dispatch end.  `bench.py` takes `frac` from `dur_allhit_glm_m1.json` while the "
+          "GEMV source hash recorded there matches."]
+    path = os.path.join(ROOT, "profiles", "glm_m1_decode_step_kernels.md")
+    with open(path, "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
+SWEEP_PROFILE_COMMAND = (
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+    "-d $REPO/gpurun_out/prof_sweep -o run -- python3 -u $REPO/bench.py --sweep-rows 2,3,4,8,16 --steps 40 "
+    "> $REPO/gpurun_out/prof_sweep.out")
+
+
+def sweep_summary(trace_csv, sweep_out):
+    """Per-M dispatch durations of a profiled --sweep-rows run.  Each M runs
+    min(steps, 4) + 3 * steps steps (warm-up, two graph replays, an eager
+    pass), in M order, and each step starts with one routing launch, so the
+    trace's launches are grouped by M by counting routing launches."""
+    import csv
+    lines = [json.loads(l) for l in open(sweep_out) if l.startswith("{")]
+    Ms = [d["M"] for d in lines]
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    n_route = sum("k_route_remap" in r["Kernel_Name"] for r in rows)
+    per = n_route // len(Ms)
+    if per * len(Ms) != n_route:
+        raise SystemExit("%d routing launches for %d values of M" % (n_route, len(Ms)))
+
+    def role(name):
+        n = name.replace("(anonymous namespace)::", "")
+        if "k_route_remap" in n:
+            return "route"
+        if "k_fill" in n:
+            return "fill"
+        if "k_combine" in n:
+            return "combine"
+        if "k_gemv" in n:
+            k0 = int(n.split("<")[1].split(",")[0])
+            return "gateup" if k0 == 6144 else "down"
+        return None
+
+    acc, names, step = {}, {}, -1
+    for r in rows:
+        k = role(r["Kernel_Name"])
+        if k is None:
+            continue
+        step += k == "route"
+        if step < 0:
+            continue
+        M = Ms[min(step // per, len(Ms) - 1)]
+        acc.setdefault((M, k), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        names.setdefault((M, k), kernel_label(r["Kernel_Name"]).replace("sc::", ""))
+    GU, DN = 14155776, 7077888     # weight bytes of one expert's gate/up and down (GLM layer)
+    L = ["# Kernel durations: all-hit GLM-shaped layer with drafted rows, M = %s (rocprofv3 kernel trace)\n"
+         % ", ".join(str(m) for m in Ms),
+         "Workload: H 6144, I 2048, 256 experts, top-8, every expert resident (S = E, preloaded), drafted rows: "
+         "rows 1..M-1 add +20 to three of row 0's top-8 logits, so about half their picks are shared; Zipf(1.1) "
+         "routing.  Per M: warm-up steps, two HIP-graph replays of the timed steps (each after a 512 MiB read "
+         "sweep, not shown) and an eager pass of the same steps: %d launches of each kernel per M.  `bench.py "
+         "--sweep-summary` groups the trace's launches by M by counting routing launches.\n" % per,
+         "Commands (`$REPO` = repository root on the GPU host):\n", "```", SWEEP_PROFILE_COMMAND,
+         "cd $REPO && python3 bench.py --sweep-summary gpurun_out/prof_sweep/run_kernel_trace.csv "
+         "gpurun_out/prof_sweep.out", "```\n",
+         "Mean (min) dispatch duration in us; weight bytes per launch are U x %d B (gate/up) and U x %d B (down), "
+         "over the mean duration in GB/s and as a fraction of 8 TB/s:\n" % (GU, DN),
+         "| M | unique experts U | route + remap | fill (exits: all hit) | gate/up | gate/up GB/s = frac | down | "
+         "down GB/s = frac | combine | graph step us (same run) |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for d in lines:
+        M, U = d["M"], d["unique_experts_per_step"]
+        mm = {k: (float(np.mean(acc[(M, k)])), float(np.min(acc[(M, k)]))) for k in
+              ("route", "fill", "gateup", "down", "combine")}
+        g, dn = mm["gateup"][0], mm["down"][0]
+        L.append("| %d | %.2f | %.2f | %.2f | %.2f (%.2f) | %.0f = %.2f | %.2f (%.2f) | %.0f = %.2f | %.2f | %.2f |"
+                 % (M, U, mm["route"][0], mm["fill"][0], g, mm["gateup"][1], U * GU / g / 1e3,
+                    U * GU / g / 1e6 / 8, dn, mm["down"][1], U * DN / dn / 1e3, U * DN / dn / 1e6 / 8,
+                    mm["combine"][0], d["us_per_step"]))
+    L += ["", "Kernels by M:"]
+    for d in lines:
+        L.append("- M = %d: gate/up `%s`, down `%s`" % (d["M"], names[(d["M"], "gateup")], names[(d["M"], "down")]))
+    path = os.path.join(ROOT, "profiles", "glm_drafted_rows_kernels.md")
+    with open(path, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+def CONFIGS_GLM():
+    from synth import CONFIGS
+    return CONFIGS["glm"]
+
+
+def trace_summary(trace_csv, stats_csv, steps_json):
     """rocprofv3 dispatch durations of each kernel over the all-hit block's timed launches.
 
     The all-hit block runs first in a default bench process: its kernels' first
@@ -899,6 +1056,7 @@ def trace_summary(trace_csv, steps_json):
         out["events_avg_us"][p] = round(float(np.mean(st["events_us"][p])), 3)
         out["launches_in_trace"][p] = len(dur)
     out["timed_launches"] = N
+    out["all_hit_warm"] = Wa
     out["kernel_names"] = st["kernel_names"]
     out["source_sha256"] = source_hash()
     out["commands"] = [
@@ -906,10 +1064,11 @@ def trace_summary(trace_csv, steps_json):
         "-d $REPO/gpurun_out/prof_bench -o run -- python3 -u $REPO/bench.py --steps 20 --warmup 5 "
         "--no-cpu-baseline --dump-steps $REPO/gpurun_out/steps_prof.json",
         "cd $REPO && python3 bench.py --trace-summary gpurun_out/prof_bench/run_kernel_trace.csv "
-        "gpurun_out/steps_prof.json"]
+        "gpurun_out/prof_bench/run_kernel_stats.csv gpurun_out/steps_prof.json"]
     print(json.dumps(out))
     with open(DUR_FILE, "w") as f:
         json.dump(out, f, indent=1)
+    trace_markdown(stats_csv, out)
 
 
 def main():
@@ -919,6 +1078,9 @@ def main():
         return
     if a.pmc_summary:
         pmc_summary(*a.pmc_summary)
+        return
+    if a.sweep_summary:
+        sweep_summary(*a.sweep_summary)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU: the decode path runs on a single MI355X "
