@@ -277,11 +277,14 @@ struct Gemv {
     uint32_t sc[R][NM][NSEG];
   };
 
-  // Row step of the task's i-th step: base + i * stride.  The loads carry no
-  // branches, so the wait before a stage's products covers that stage only
-  // (with one branch per row the compiler waited for every outstanding load,
-  // the next stage's included): a stage past the end of the run re-reads the
-  // run's last row step, and process() stores nothing for it.
+  // Row step of the task's i-th step: base + i * stride.  The loads of one
+  // stage carry no branches (with one branch per row the compiler waited for
+  // every outstanding load before the stage's first product): a row step past
+  // the end of the run re-reads the run's last row step, and process() stores
+  // nothing for it.  The loop below skips the next stage's loads at the end of
+  // a run, so the compiler waits for them too before the current stage's last
+  // products; a branch-free steady state that keeps them in flight measured
+  // slower (more registers: two wavefronts per SIMD for gate/up).
   __device__ static __forceinline__ void load(Buf& b, const uint8_t* code_base, const uint8_t* scale_base,
                                               int i, int n, int base, int stride, int rsub, int up_row0) {
 #pragma unroll
