@@ -158,7 +158,7 @@ def cpu_baseline(glm_logits, glm_xs, start, nsteps):
 
     value: full fp64 step (routing, LRU, dequant, expert math) on `nsteps`
     consecutive one-row GLM steps.  Beside it: the tiny layer's full step on all
-    its 64 steps, and bookkeeping alone (routing + slot bookkeeping) per
+    its 64 steps, the Flash stack's expert math on one fixed layer-step, and bookkeeping alone (routing + slot bookkeeping) per
     layer-step on every workload (the stacks on a sample of layers)."""
     from oracle import OracleLayer, route
     from oracle.lru import SlotState
@@ -208,6 +208,21 @@ def cpu_baseline(glm_logits, glm_xs, start, nsteps):
                 "sample": "%d of %d layers x %d steps" % (layers, cfg.n_layers, steps) if cfg.n_layers > 1
                           else "all %d steps" % steps}
 
+    # the Flash stack's expert math (M = 8) on a fixed sample: step 63 of layer 0
+    from oracle.expert import layer_output
+    fl = CONFIGS["flash"]
+    fl_us = []
+    for layer in (0,):
+        lg, rows = routing_trace(fl, layer, steps=64)
+        M = int(rows[63])
+        ids, w = route(lg[63, :M], fl.top_k)
+        fb = {e: expert_blob(fl, layer, e) for e in sorted(set(int(v) for v in ids.reshape(-1)))}
+        xb = activations(fl, layer, 63, M)
+        gsf = global_scales(fl, layer, "unit")
+        t0 = time.perf_counter()
+        layer_output(ids, w, xb, lambda e: fb[e], gsf, fl.hidden, fl.inter)
+        fl_us.append((time.perf_counter() - t0) * 1e6)
+
     bk = {"tiny": bookkeeping(tiny, 1, tiny.steps), "glm": bookkeeping(glm, 1, glm.steps),
           "glm_draft": bookkeeping(CONFIGS["glm_draft"], 1, CONFIGS["glm_draft"].steps),
           "glm_stack": bookkeeping(CONFIGS["glm_stack"], 4, CONFIGS["glm_stack"].steps),
@@ -218,6 +233,10 @@ def cpu_baseline(glm_logits, glm_xs, start, nsteps):
                   "dequant, expert math); blob generation excluded" % nsteps,
         "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
         "tiny_full_step_us": {"us_per_layer_step": round(tiny_full * 1e6, 1), "sample": "all 64 steps"},
+        "flash_expert_math_us": {"us_per_layer_step": round(float(np.mean(fl_us)), 1),
+                                 "sample": "step 63 of layer 0 (M = 8): dequant and expert math of the "
+                                           "step's unique experts, blob generation excluded; the GLM stack's "
+                                           "layers have the GLM layer's shape, whose full step is `value`"},
         "bookkeeping_only": bk,
     }
 
