@@ -250,9 +250,9 @@ struct XRed {
 // Streaming GEMV.  Each unique expert's row steps are split into `wpu`
 // contiguous runs, one per wavefront (task); a wavefront keeps the operand
 // slices of up to MR picks in registers and walks its run R row steps at a
-// time with the next R steps' code and scale loads issued before the current
-// ones are consumed (register double buffering), so every wavefront always has
-// two groups of loads in flight.
+// time, issuing the next R steps' code and scale loads (a second register
+// set) before it sums the current ones; the compiler's waits let those loads
+// overlap the current steps' first products (see load()).
 //
 // SINGLE: a one-row step.  Its k picks are k distinct experts, so U = k and
 // pick u is unique expert u (the remap's CSR lists are the identity): the
@@ -487,13 +487,13 @@ struct Gemv {
 
 // Streaming GEMVs for steps of two to four rows.  The weights stream as in
 // the one-row kernels (a lane owns 32 K-elements per 2048-wide chunk; the next
-// row steps' loads are in flight while the current ones are summed), each
+// row steps' loads are issued before the current ones are summed), each
 // chunk's codes are widened once (gate/up to bf16 pairs, down to fp32), and
-// every pick of the expert is computed from them.  A cached step of M rows gives an expert at most M picks (a row's
-// top-k experts are distinct), so the operand rows (x or h) of an expert's at
-// most kSharedPicks picks sit in LDS, loaded once per block task and shared by
-// the block's four wavefronts: a block task is a run of one expert's row
-// steps, split among the wavefronts.  A row's products, its block-scale
+// every pick of the expert is computed from them.  A step of M rows gives an
+// expert at most M picks (a row's top-k experts are distinct), so the operand
+// rows (x or h) of an expert's at most kSharedPicks picks sit in LDS, loaded
+// once per block task and shared by the block's four wavefronts: a block task
+// is a run of one expert's row steps, split among the wavefronts.  A row's products, its block-scale
 // products and its cross-lane sums are those of the one-row kernel, in the
 // same order, so each row's bits do not depend on how many rows the step has.
 // In LDS, operand piece v (16 bytes) of lane `seg` in a chunk sits in slot
@@ -1522,7 +1522,7 @@ GemvFn pick_shared(int K) {
     default: return nullptr;
   }
 }
-// A cached step of 2 .. kSharedPicks rows gives each expert at most M picks.
+// A step of 2 .. kSharedPicks rows gives each expert at most M picks (cached or bypass).
 bool shared_step(int M, int group) { return M >= 2 && M <= kSharedPicks && group < 0; }
 
 }  // namespace
