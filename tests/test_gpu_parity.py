@@ -459,7 +459,7 @@ def test_batch_invariant_rows(shape):
         g = CONFIGS["glm"]
         cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 32, rows=24, steps=1, seed=g.seed)
     elif shape == "h1024_i512":
-        # 16- and 32-lane row groups: the two-pick down kernel sums eight values per row group
+        # 16- and 32-lane row groups: the multi-row down kernels sum eight values per row group
         cfg = WorkloadConfig("h1024_i512", 1024, 512, 32, 4, 32, rows=24, steps=1, seed=71)
     log("batch invariance: %s" % shape)
     E = cfg.n_experts

@@ -18,8 +18,8 @@ fp32 combine of its section "A correction first"):
 
 Layer: GLM shapes (H 6144, I 2048), 8 experts, top-1, 5 slots (misses go
 through the fill; steps with more unique experts than slots read the others
-from the host store), steps of 1 to 16 rows, so the one-row, two-pick and
-matrix-core kernels all run.
+from the host store), steps of 1 to 16 rows, so the one-row, shared-operand
+streaming and matrix-core kernels all run.
 """
 import numpy as np
 import pytest
