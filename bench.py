@@ -33,7 +33,7 @@ METRIC = "µs per MoE layer-step (M=1) + achieved HBM GB/s vs peak; LRU hit rate
 HBM_PEAK_GBS = 8000.0
 PHASES = ("route_remap", "fill", "gateup", "down", "combine")
 # kernels of a one-row GLM step, as rocprofv3 names them (template arguments included)
-KERNEL_NAMES = {"route_remap": "k_route_remap<4>", "fill": "k_fill(", "gateup": "k_gemv<6144, 1, 1, true, true>",
+KERNEL_NAMES = {"route_remap": "k_route_remap<4, 256>", "fill": "k_fill(", "gateup": "k_gemv<6144, 1, 1, true, true>",
                 "down": "k_gemv<2048, 1, 4, false, true>", "combine": "k_combine("}
 CACHE_WARMUP = 32          # steps that fill the cache before anything is measured
 ALL_HIT_WARM = 4           # untimed all-hit steps before the timed ones

@@ -1,5 +1,6 @@
 // Router top-k, routing weights and the fused expert-id -> slot remap with
-// batch-LRU victim choice, in one workgroup of four wavefronts.
+// batch-LRU victim choice, in one workgroup: four wavefronts, or eight for a
+// step of many picks (each wavefront routes one row at a time).
 //
 // Method: the slot cache of page "GLM 5.3 Testing: HBM Expert Allocation"
 // (section "What the slot cache is": ids are mapped to slots on the device
@@ -31,6 +32,11 @@
 
 namespace sc {
 namespace {
+
+// Steps of at least kRouteWidePicks picks (eight rows of top-8) route on eight
+// wavefronts: twice the rows in flight, at the cost of wider barriers.
+constexpr int kRouteWideThreads = 512;
+constexpr int kRouteWidePicks = 64;
 
 __device__ __forceinline__ uint64_t order_key(float z, int e) {
   // Larger key = earlier pick: logit descending, then expert id ascending.
@@ -116,7 +122,8 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Exclusive rank of `pred` among the block's threads in thread order.
+// Exclusive rank of `pred` among the block's NT threads in thread order.
+template <int NT>
 __device__ __forceinline__ int block_rank(bool pred, int* s_wc, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint64_t mask = __ballot(pred);
@@ -125,7 +132,7 @@ __device__ __forceinline__ int block_rank(bool pred, int* s_wc, int* total) {
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kRouteThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     int c = s_wc[w];
     if (w < wave) base += c;
     tot += c;
@@ -135,7 +142,8 @@ __device__ __forceinline__ int block_rank(bool pred, int* s_wc, int* total) {
   return base + in_wave;
 }
 
-// Exclusive scan of s_in[0..n) into s_out (n <= 4 * blockDim); returns the total.
+// Exclusive scan of s_in[0..n) into s_out (n <= 4 * NT); returns the total.
+template <int NT>
 __device__ __forceinline__ int block_scan(const int* s_in, int* s_out, int n, int* s_wc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int v[4], sum = 0;
@@ -155,7 +163,7 @@ __device__ __forceinline__ int block_scan(const int* s_in, int* s_out, int n, in
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kRouteThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     if (w < wave) base += s_wc[w];
     tot += s_wc[w];
   }
@@ -240,10 +248,10 @@ __device__ __forceinline__ void route_row(const float (&z)[EPL], int E, int k, i
   *logit = my_ord == 1u ? __uint_as_float(0x7FC00000u) : __uint_as_float(zb);
 }
 
-template <int EPL>
-__global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
-  constexpr int SPT = kMaxSlots / kRouteThreads;   // slots per thread
-  constexpr int XPT = kMaxExperts / kRouteThreads; // experts per thread
+template <int EPL, int NT>
+__global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
+  constexpr int SPT = kMaxSlots / NT;   // slots per thread
+  constexpr int XPT = kMaxExperts / NT; // experts per thread
   __shared__ __attribute__((aligned(16))) int s_pick[kMaxPicks];
   __shared__ int s_first[kMaxExperts];   // first pick position per expert; later pick counts
   __shared__ int s_last[kMaxExperts];
@@ -256,8 +264,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   __shared__ int s_s2e[kMaxSlots];
   __shared__ long long s_key[kMaxSlots]; // snapshot of the clock, then candidate keys
   __shared__ uint8_t s_ref[kMaxSlots];
-  __shared__ int s_wc[kRouteThreads / 64];
-  __shared__ unsigned long long s_wmin[kRouteThreads / 64];
+  __shared__ int s_wc[NT / 64];
+  __shared__ unsigned long long s_wmin[NT / 64];
   __shared__ int s_nevict;
 
   span_start(a.span);
@@ -279,18 +287,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   int64_t r_key[SPT];
 #pragma unroll
   for (int q = 0; q < XPT; ++q) {
-    const int e = tid + q * kRouteThreads;
+    const int e = tid + q * NT;
     r_e2s[q] = e < E ? a.L.e2s[e] : -1;
   }
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
-    const int sl = tid + q * kRouteThreads;
+    const int sl = tid + q * NT;
     r_s2e[q] = sl < S ? a.L.s2e[sl] : -1;
     r_key[q] = sl < S ? a.L.key[sl] : -1;
   }
 
   // ---- router: one row per wavefront, up to four rows' logits in flight ----
-  constexpr int NW = kRouteThreads / 64;
+  constexpr int NW = NT / 64;
   constexpr int RD = 4;                         // rows in flight per wavefront
   float zr[RD][EPL];
 #pragma unroll
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   }
 #pragma unroll
   for (int q = 0; q < XPT; ++q) {
-    const int e = tid + q * kRouteThreads;
+    const int e = tid + q * NT;
     if (e < E) {
       s_e2s[e] = r_e2s[q];
       s_first[e] = INT_MAX;
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   }
 #pragma unroll
   for (int q = 0; q < SPT; ++q) {
-    const int sl = tid + q * kRouteThreads;
+    const int sl = tid + q * NT;
     if (sl < S) {
       s_s2e[sl] = r_s2e[q];
       s_key[sl] = (long long)r_key[q];
@@ -350,18 +358,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   __syncthreads();
 
   // ---- unique experts in first-occurrence order ----------------------------
-  for (int p = tid; p < P; p += kRouteThreads) {
+  for (int p = tid; p < P; p += NT) {
     atomicMin(&s_first[s_pick[p]], p);
     atomicMax(&s_last[s_pick[p]], p);
   }
   __syncthreads();
   int U = 0;
-  for (int base = 0; base < P; base += kRouteThreads) {
+  for (int base = 0; base < P; base += NT) {
     const int p = base + tid;
     const int e = p < P ? s_pick[p] : 0;
     const bool f = p < P && s_first[e] == p;
     int tot;
-    const int r = block_rank(f, s_wc, &tot);
+    const int r = block_rank<NT>(f, s_wc, &tot);
     if (f) {
       s_uexp[U + r] = e;
       s_uidx[e] = U + r;
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   const int64_t B = a.sh.blob;
   const int Pn = a.L.P;
   // ---- residency against the slot map (bypass steps use it too) -----------
-  for (int u = tid; u < U; u += kRouteThreads) {
+  for (int u = tid; u < U; u += NT) {
     int sl = s_e2s[s_uexp[u]];
     if (sl < -1 || sl >= S) {
       atomicOr(a.L.error, 1u);
@@ -383,13 +391,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   }
   __syncthreads();
   int nmiss = 0, npin = 0;
-  for (int base = 0; base < U; base += kRouteThreads) {
+  for (int base = 0; base < U; base += NT) {
     const int u = base + tid;
     const bool ms = u < U && s_uslot[u] < 0;
     const bool pn = u < U && s_uslot[u] >= 0 && s_uslot[u] < Pn;
     int tot, tot_pin;
-    const int r = block_rank(ms, s_wc, &tot);
-    (void)block_rank(pn, s_wc, &tot_pin);
+    const int r = block_rank<NT>(ms, s_wc, &tot);
+    (void)block_rank<NT>(pn, s_wc, &tot_pin);
     // a miss stores its rank among misses; a resident expert -1 - its rank
     // among resident ones (r counts the misses before u in either case)
     if (u < U) s_umiss[u] = ms ? nmiss + r : -1 - (u - (nmiss + r));
@@ -401,9 +409,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
   if (!bypass) {
     if (nmiss > 0) {
       // ---- victims: the nmiss least (key, slot) among slots not hit ---------
-      for (int sl = tid; sl < S; sl += kRouteThreads) s_ref[sl] = 0;
+      for (int sl = tid; sl < S; sl += NT) s_ref[sl] = 0;
       __syncthreads();
-      for (int u = tid; u < U; u += kRouteThreads)
+      for (int u = tid; u < U; u += NT)
         if (s_uslot[u] >= 0) s_ref[s_uslot[u]] = 1;
       __syncthreads();
       if (nmiss <= 8) {
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
         uint64_t ck[SPT];
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
-          const int sl = tid + q * kRouteThreads;
+          const int sl = tid + q * NT;
           ck[q] = (sl >= Pn && sl < S && !s_ref[sl]) ? (((uint64_t)(s_key[sl] + 2) << 11) | (uint64_t)sl) : ~0ull;
         }
         for (int i = 0; i < nmiss; ++i) {
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
           __syncthreads();
           uint64_t g = s_wmin[0];
 #pragma unroll
-          for (int w = 1; w < kRouteThreads / 64; ++w) g = s_wmin[w] < g ? s_wmin[w] : g;
+          for (int w = 1; w < NT / 64; ++w) g = s_wmin[w] < g ? s_wmin[w] : g;
 #pragma unroll
           for (int q = 0; q < SPT; ++q)
             if (ck[q] == g) ck[q] = ~0ull;
@@ -433,12 +441,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
         }
       } else {
         // many misses: rank every candidate by (key, slot)
-        for (int sl = tid; sl < S; sl += kRouteThreads) {
+        for (int sl = tid; sl < S; sl += NT) {
           if (s_ref[sl] || sl < Pn) s_key[sl] = (long long)LLONG_MAX;
           s_victim[sl] = -1;
         }
         __syncthreads();
-        for (int sl = tid; sl < S; sl += kRouteThreads) {
+        for (int sl = tid; sl < S; sl += NT) {
           if (s_ref[sl] || sl < Pn) continue;
           const long long ks = s_key[sl];
           int r = 0;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       }
       __syncthreads();
       // ---- apply the misses: evict, remap, log, queue the fills ------------
-      for (int u = tid; u < U; u += kRouteThreads) {
+      for (int u = tid; u < U; u += NT) {
         const int i = s_umiss[u];
         if (i < 0) continue;
         const int e = s_uexp[u];
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     }
     // ---- stamp the clock, publish slot pointers and the resident-first order
     const int nres = U - nmiss;
-    for (int u = tid; u < U; u += kRouteThreads) {
+    for (int u = tid; u < U; u += NT) {
       const int sl = s_uslot[u], i = s_umiss[u];
       a.W.uniq_order[i >= 0 ? nres + i : -1 - i] = u;
       if (sl < 0) {
@@ -506,7 +514,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     // one is copied into staging blob i % G by group i / G.  uniq_order lists
     // the resident experts, then the staged ones in staging order.
     const int G = a.W.stage_n, nres = U - nmiss;
-    for (int u = tid; u < U; u += kRouteThreads) {
+    for (int u = tid; u < U; u += NT) {
       const int sl = s_uslot[u], i = s_umiss[u];
       if (sl >= 0) {
         a.W.uniq_ptr[u] = a.L.slots + (size_t)sl * B;
@@ -521,18 +529,18 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     }
   } else {
     // bypass: resident experts from their slots, the others read in place from the backing store
-    for (int u = tid; u < U; u += kRouteThreads) {
+    for (int u = tid; u < U; u += NT) {
       const int sl = s_uslot[u];
       a.W.uniq_ptr[u] = sl >= 0 ? a.L.slots + (size_t)sl * B : a.L.backing + (size_t)s_uexp[u] * B;
       a.W.uniq_order[u] = u;
     }
   }
-  for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_expert[u] = s_uexp[u];
+  for (int u = tid; u < U; u += NT) a.W.uniq_expert[u] = s_uexp[u];
 
   // ---- picks grouped by unique expert (CSR), ascending pick order ---------
   if (U == P) {
     // every pick is its own unique expert, in pick order
-    for (int p = tid; p < P; p += kRouteThreads) {
+    for (int p = tid; p < P; p += NT) {
       a.W.pick_u[p] = p;
       a.W.uniq_picks[p] = p;
       a.W.uniq_off[p] = p;
@@ -541,16 +549,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
     int* s_cnt = s_first;   // free after the unique pass
     int* s_off = s_umiss;   // free after the miss pass
     __syncthreads();
-    for (int u = tid; u < U; u += kRouteThreads) s_cnt[u] = 0;
+    for (int u = tid; u < U; u += NT) s_cnt[u] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += kRouteThreads) {
+    for (int p = tid; p < P; p += NT) {
       const int u = s_uidx[s_pick[p]];
       atomicAdd(&s_cnt[u], 1);
       a.W.pick_u[p] = u;
     }
     __syncthreads();
-    block_scan(s_cnt, s_off, U, s_wc);
-    for (int p = tid; p < P; p += kRouteThreads) {
+    block_scan<NT>(s_cnt, s_off, U, s_wc);
+    for (int p = tid; p < P; p += NT) {
       const int e = s_pick[p];
       // rank of p among the picks of e: earlier picks of e, four per LDS read
       int r = 0, q = 0;
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
       for (; q < p; ++q) r += s_pick[q] == e;
       a.W.uniq_picks[s_off[s_uidx[e]] + r] = p;
     }
-    for (int u = tid; u < U; u += kRouteThreads) a.W.uniq_off[u] = s_off[u];
+    for (int u = tid; u < U; u += NT) a.W.uniq_off[u] = s_off[u];
   }
 
   if (tid == 0) {
@@ -595,6 +603,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_remap(RouteArgs a) {
 
 }  // namespace
 
+template <int NT>
+static hipError_t launch_route_nt(int epl, const RouteArgs& a, hipStream_t st, KEvents ev) {
+  const dim3 g(1), b(NT);
+  if (epl <= 1) return sc_launch(k_route_remap<1, NT>, g, b, st, ev, a);
+  if (epl <= 2) return sc_launch(k_route_remap<2, NT>, g, b, st, ev, a);
+  if (epl <= 4) return sc_launch(k_route_remap<4, NT>, g, b, st, ev, a);
+  if (epl <= 8) return sc_launch(k_route_remap<8, NT>, g, b, st, ev, a);
+  return sc_launch(k_route_remap<16, NT>, g, b, st, ev, a);
+}
+
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
                         const float* logits, int M, hipStream_t st, KEvents ev) {
   RouteArgs a;
@@ -605,12 +623,8 @@ hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
   a.M = M;
   a.span = ev.span_for(1);
   const int epl = (sh.E + 63) / 64;
-  const dim3 g(1), b(kRouteThreads);
-  if (epl <= 1) return sc_launch(k_route_remap<1>, g, b, st, ev, a);
-  if (epl <= 2) return sc_launch(k_route_remap<2>, g, b, st, ev, a);
-  if (epl <= 4) return sc_launch(k_route_remap<4>, g, b, st, ev, a);
-  if (epl <= 8) return sc_launch(k_route_remap<8>, g, b, st, ev, a);
-  return sc_launch(k_route_remap<16>, g, b, st, ev, a);
+  if (M * sh.k >= kRouteWidePicks) return launch_route_nt<kRouteWideThreads>(epl, a, st, ev);
+  return launch_route_nt<kRouteThreads>(epl, a, st, ev);
 }
 
 }  // namespace sc
