@@ -420,7 +420,7 @@ def test_misses_fill_their_slots_exactly(shape):
     sc.close()
 
 
-def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True):
+def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True, identical=False):
     """Max number of rows whose output differs (bitwise) from the same row run as a one-row step."""
     torch = torch_cuda()
     rng = np.random.default_rng(seed)
@@ -428,7 +428,9 @@ def _rows_vs_single(cfg, sc_multi, sc_single, Ms, seed, drafted=True):
     bad = {}
     for t, M in enumerate(Ms):
         z = rng.standard_normal((M, E)).astype(np.float32)
-        if drafted:                   # later rows share picks with row 0 (draft / verify rounds)
+        if identical:                 # every row routes alike: each expert gets M picks
+            z[:] = z[0]
+        elif drafted:                 # later rows share picks with row 0 (draft / verify rounds)
             top = np.argsort(-z[0])[:cfg.top_k]
             for m in range(1, M):
                 z[m, rng.choice(top, min(3, len(top)), replace=False)] += 20.0
@@ -479,6 +481,44 @@ def test_batch_invariant_rows(shape):
     assert inv.stats(0)["bypass_steps"] == 1      # M = 24 > 16
     for sc in (inv, dflt, one):
         sc.close()
+
+
+def test_identical_rows_fill_every_pick_column():
+    """Steps whose rows all route alike give each picked expert as many picks as
+    the step has rows: 4 on the shared-operand streaming kernels, 8 and 16 on
+    the matrix-core kernels, whose pick columns are then all live.  Outputs
+    match the oracle; at 4 rows (streaming) and, with SC_FLAG_BATCH_INVARIANT,
+    at 8 and 16 rows every row is bit-equal to the same row decoded alone."""
+    g = CONFIGS["glm"]
+    cfg = WorkloadConfig("glm32", g.hidden, g.inter, 32, g.top_k, 32, rows=16, steps=9, seed=g.seed)
+    E = cfg.n_experts
+    log("identical rows: glm32, M in 4, 8, 16")
+    sc = make_cache(cfg, max_rows=16)
+    orc = _oracle_layer(cfg, cfg.slots)
+    rng = np.random.default_rng(29)
+    Ms = [4, 8, 16, 16, 8, 4, 16, 4, 8]
+    zs = [np.repeat(rng.standard_normal((1, E)).astype(np.float32), 16, axis=0) for _ in Ms]
+    worst = _run_trace(cfg, sc, orc, len(Ms), lambda t: Ms[t], lambda t: zs[t])
+    st = sc.stats(0)
+    log("identical rows: worst rel L2 %.3g, stats %s" % (worst, st))
+    assert st["bypass_steps"] == 0 and st["picks"] == sum(M * cfg.top_k for M in Ms)
+    assert st["lookups"] == len(Ms) * cfg.top_k          # one lookup per unique expert
+    sc.close()
+
+    from hbm_expert_slot_amd import binding as B
+    m_stream = min(B.SC_MFMA_MIN_ROWS_GATEUP, B.SC_MFMA_MIN_ROWS_DOWN)
+    dflt = make_cache(cfg, n_layers=1, slots=[E], max_rows=16)
+    inv = make_cache(cfg, n_layers=1, slots=[E], max_rows=16, batch_invariant=True)
+    one = make_cache(cfg, n_layers=1, slots=[E], max_rows=1)
+    for c in (dflt, inv, one):
+        c.preload(0)
+    bad_dflt = _rows_vs_single(cfg, dflt, one, [M for M in (2, 3, 4) if M < m_stream], seed=5, identical=True)
+    bad_inv = _rows_vs_single(cfg, inv, one, [4, 8, 16], seed=5, identical=True)
+    log("identical rows differing from one-row results: default %s, invariant %s" % (bad_dflt, bad_inv))
+    assert all(v == 0 for v in bad_dflt.values()), bad_dflt
+    assert all(v == 0 for v in bad_inv.values()), bad_inv
+    for c in (dflt, inv, one):
+        c.close()
 
 
 @pytest.mark.parametrize("shape", ["tiny", "glm32"])
