@@ -33,7 +33,7 @@ METRIC = "µs per MoE layer-step (M=1) + achieved HBM GB/s vs peak; LRU hit rate
 HBM_PEAK_GBS = 8000.0
 PHASES = ("route_remap", "fill", "gateup", "down", "combine")
 # kernels of a one-row GLM step, as rocprofv3 names them (template arguments included)
-KERNEL_NAMES = {"route_remap": "k_route_remap<4, 256>", "fill": "k_fill(", "gateup": "k_gemv<6144, 1, 1, true, true>",
+KERNEL_NAMES = {"route_remap": "k_route_one<4, 4>", "fill": "k_fill(", "gateup": "k_gemv<6144, 1, 1, true, true>",
                 "down": "k_gemv<2048, 1, 4, false, true>", "combine": "k_combine("}
 CACHE_WARMUP = 32          # steps that fill the cache before anything is measured
 ALL_HIT_WARM = 4           # untimed all-hit steps before the timed ones
@@ -986,14 +986,14 @@ def sweep_summary(trace_csv, sweep_out):
     lines = [json.loads(l) for l in open(sweep_out) if l.startswith("{")]
     Ms = [d["M"] for d in lines]
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
-    n_route = sum("k_route_remap" in r["Kernel_Name"] for r in rows)
+    n_route = sum("k_route_" in r["Kernel_Name"] for r in rows)
     per = n_route // len(Ms)
     if per * len(Ms) != n_route:
         raise SystemExit("%d routing launches for %d values of M" % (n_route, len(Ms)))
 
     def role(name):
         n = name.replace("(anonymous namespace)::", "")
-        if "k_route_remap" in n:
+        if "k_route_" in n:
             return "route"
         if "k_fill" in n:
             return "fill"

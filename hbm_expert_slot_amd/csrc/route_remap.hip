@@ -1,6 +1,7 @@
 // Router top-k, routing weights and the fused expert-id -> slot remap with
 // batch-LRU victim choice, in one workgroup: four wavefronts, or eight for a
-// step of many picks (each wavefront routes one row at a time).
+// step of many picks (each wavefront routes one row at a time), or a single
+// wavefront for a one-row step.
 //
 // Method: the slot cache of page "GLM 5.3 Testing: HBM Expert Allocation"
 // (section "What the slot cache is": ids are mapped to slots on the device
@@ -37,6 +38,9 @@ namespace {
 // wavefronts: twice the rows in flight, at the cost of wider barriers.
 constexpr int kRouteWideThreads = 512;
 constexpr int kRouteWidePicks = 64;
+// One-row steps of at most kRouteOneMaxK picks that cannot bypass route on one
+// wavefront (k_route_one); the victim search takes one wavefront minimum per miss.
+constexpr int kRouteOneMaxK = 16;
 
 __device__ __forceinline__ uint64_t order_key(float z, int e) {
   // Larger key = earlier pick: logit descending, then expert id ascending.
@@ -248,6 +252,23 @@ __device__ __forceinline__ void route_row(const float (&z)[EPL], int E, int k, i
   *logit = my_ord == 1u ? __uint_as_float(0x7FC00000u) : __uint_as_float(zb);
 }
 
+// Routing weight of lane j's pick (j < k): softmax over the k chosen logits,
+// in the limits for non-finite picks (+inf picks share the weight, a NaN or
+// -inf leading logit gives every pick 1/k).  zj is route_row's logit.
+__device__ __forceinline__ float pick_weight(float zj, int k, int lane) {
+  const bool act = lane < k;
+  if (!act) zj = 0.0f;
+  const bool is_nan = zj != zj;
+  const bool pinf = act && zj == INFINITY;
+  const int npinf = __popcll(__ballot(pinf));
+  const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
+  if (npinf > 0) return pinf ? 1.0f / (float)npinf : 0.0f;
+  if (z0 != z0 || z0 == -INFINITY) return 1.0f / (float)k;
+  const float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
+  const float sum = wave_sum_f32(ex);
+  return ex / sum;
+}
+
 template <int EPL, int NT>
 __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
   constexpr int SPT = kMaxSlots / NT;   // slots per thread
@@ -313,24 +334,8 @@ __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
       float zj;
       route_row<EPL>(zr[d], E, k, lane, &my_e, &zj);
       if (m + RD * NW < M) load_row<EPL>(a.logits + (size_t)(m + RD * NW) * E, E, lane, zr[d]);
-      // weights: softmax over the k chosen logits (limits for non-finite picks)
-      const bool act = lane < k;
-      if (!act) zj = 0.0f;
-      const bool is_nan = zj != zj;
-      const bool pinf = act && zj == INFINITY;
-      const int npinf = __popcll(__ballot(pinf));
-      const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zj), 0));
-      float w;
-      if (npinf > 0) {
-        w = pinf ? 1.0f / (float)npinf : 0.0f;
-      } else if (z0 != z0 || z0 == -INFINITY) {
-        w = 1.0f / (float)k;
-      } else {
-        const float ex = (act && !is_nan) ? expf(zj - z0) : 0.0f;
-        const float sum = wave_sum_f32(ex);
-        w = ex / sum;
-      }
-      if (act) {
+      const float w = pick_weight(zj, k, lane);
+      if (lane < k) {
         s_pick[m * k + lane] = my_e;
         a.W.pick_expert[m * k + lane] = my_e;
         a.W.pick_w[m * k + lane] = w;
@@ -601,6 +606,181 @@ __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
   span_end(a.span);
 }
 
+// One-row steps on one wavefront.  A row's k picks are distinct experts, so
+// the unique experts are the picks in rank order, every expert has one pick
+// and the CSR lists are the identity; with k <= S - P the step cannot bypass.
+// Lane j < k owns pick j.  Without block barriers or the general kernel's
+// unique and CSR passes, the step's critical path is the logits load, the
+// top-k rounds and the stores; the bookkeeping rules and every value written
+// are the general kernel's.
+template <int EPL, int SPL>
+__global__ __launch_bounds__(64) void k_route_one(RouteArgs a) {
+  __shared__ int s_e2s[kMaxExperts];
+  __shared__ int s_s2e[kMaxSlots];
+  __shared__ uint8_t s_ref[kMaxSlots];
+
+  span_start(a.span);
+  const int lane = threadIdx.x;
+  const int E = a.sh.E, k = a.sh.k, S = a.L.S, Pn = a.L.P;
+  const int64_t t = *a.L.step;
+  const uint64_t ev_head = *a.L.ev_head;
+  uint64_t cnt[C_N];
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < C_N; ++c) cnt[c] = a.L.counters[c];
+  }
+  // Every load is issued unconditionally (indices clamped into range, the
+  // values past the end replaced afterwards): loads under a branch let the
+  // compiler wait for each one inside its branch, one memory latency apiece.
+  int r_e2s[EPL], r_s2e[SPL];
+  int64_t r_key[SPL];
+  float z[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    const int e = min(lane + 64 * q, E - 1);
+    r_e2s[q] = a.L.e2s[e];
+    z[q] = a.logits[e];
+  }
+#pragma unroll
+  for (int q = 0; q < SPL; ++q) {
+    const int sl = min(lane + 64 * q, S - 1);
+    r_s2e[q] = a.L.s2e[sl];
+    r_key[q] = a.L.key[sl];
+  }
+#pragma unroll
+  for (int q = 0; q < EPL; ++q)
+    if (lane + 64 * q >= E) {
+      r_e2s[q] = -1;
+      z[q] = 0.0f;
+    }
+#pragma unroll
+  for (int q = 0; q < SPL; ++q)
+    if (lane + 64 * q >= S) {
+      r_s2e[q] = -1;
+      r_key[q] = -1;
+    }
+  int e;
+  float zj;
+  route_row<EPL>(z, E, k, lane, &e, &zj);
+  const float w = pick_weight(zj, k, lane);
+  const bool act = lane < k;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q)
+    if (lane + 64 * q < E) s_e2s[lane + 64 * q] = r_e2s[q];
+#pragma unroll
+  for (int q = 0; q < SPL; ++q)
+    if (lane + 64 * q < S) {
+      s_s2e[lane + 64 * q] = r_s2e[q];
+      s_ref[lane + 64 * q] = 0;
+    }
+  __syncthreads();
+
+  // residency; a miss's rank among misses, a hit's among hits, in pick order
+  int sl = act ? s_e2s[e] : -1;
+  if (act && (sl < -1 || sl >= S)) {
+    atomicOr(a.L.error, 1u);
+    sl = -1;
+  }
+  const bool miss = act && sl < 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t mmask = __ballot(miss);
+  const int nmiss = __popcll(mmask);
+  const int mrank = __popcll(mmask & below);
+  const int nres = k - nmiss;
+  int nevict = 0;
+  if (nmiss > 0) {
+    // victims: the nmiss least (key, slot) among unpinned slots not hit;
+    // packed as (key + 2, slot) with keys >= -1, ~0 meaning "none"
+    if (act && !miss) s_ref[sl] = 1;
+    __syncthreads();
+    uint64_t ck[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+      const int c = lane + 64 * q;
+      ck[q] = (c >= Pn && c < S && !s_ref[c]) ? (((uint64_t)(r_key[q] + 2) << 11) | (uint64_t)c) : ~0ull;
+    }
+    int my_victim = -1;
+    for (int i = 0; i < nmiss; ++i) {
+      uint64_t loc = ~0ull;
+#pragma unroll
+      for (int q = 0; q < SPL; ++q) loc = ck[q] < loc ? ck[q] : loc;
+      const uint64_t g = wave_reduce_u64<false>(loc);
+#pragma unroll
+      for (int q = 0; q < SPL; ++q)
+        if (ck[q] == g) ck[q] = ~0ull;
+      if (lane == i) my_victim = g == ~0ull ? -1 : (int)(g & 0x7FFull);
+    }
+    const int v = __shfl(my_victim, miss ? mrank : 0);
+    int old = -1;
+    if (miss) {
+      if (v < 0 || v >= S) {
+        // no victim (cannot happen while the maps are consistent): read this
+        // expert from the backing store and make the fill skip it
+        atomicOr(a.L.error, 4u);
+        a.W.miss_src[mrank] = nullptr;
+        a.W.miss_dst[mrank] = nullptr;
+      } else {
+        old = s_s2e[v];
+        if (old >= E) {
+          atomicOr(a.L.error, 2u);
+          old = -1;
+        }
+        if (old >= 0) a.L.e2s[old] = -1;
+        a.L.e2s[e] = v;
+        a.L.s2e[v] = e;
+        sl = v;
+        sc_event ev;
+        ev.step = t;
+        ev.expert = e;
+        ev.slot = v;
+        ev.evicted = old;
+        ev.reserved = 0;
+        a.L.events[(ev_head + (uint64_t)mrank) % (uint64_t)a.L.ev_cap] = ev;
+        a.W.miss_src[mrank] = a.L.backing + (size_t)e * a.sh.blob;
+        a.W.miss_dst[mrank] = a.L.slots + (size_t)v * a.sh.blob;
+      }
+    }
+    nevict = __popcll(__ballot(old >= 0));
+  }
+  if (act) {
+    const int64_t B = a.sh.blob;
+    a.W.pick_expert[lane] = e;
+    a.W.pick_w[lane] = w;
+    a.W.uniq_order[miss ? nres + mrank : lane - mrank] = lane;
+    if (sl >= 0) {
+      a.L.key[sl] = t * (int64_t)(kCachedRows * k) + (int64_t)lane;
+      a.W.uniq_ptr[lane] = a.L.slots + (size_t)sl * B;
+    } else {
+      a.W.uniq_ptr[lane] = a.L.backing + (size_t)e * B;
+    }
+    a.W.uniq_expert[lane] = e;
+    a.W.pick_u[lane] = lane;
+    a.W.uniq_picks[lane] = lane;
+    a.W.uniq_off[lane] = lane;
+  }
+  if (lane == 0) {
+    a.W.uniq_off[k] = k;
+    a.W.hdr[H_UNIQUE] = k;
+    a.W.hdr[H_MISS] = nmiss;
+    a.W.hdr[H_BYPASS] = 0;
+    a.W.hdr[H_ROWS] = 1;
+    a.W.hdr[H_RESIDENT] = nres;
+    a.W.hdr[H_STAGED] = 0;
+    cnt[C_STEPS] += 1;
+    cnt[C_PICKS] += (uint64_t)k;
+    cnt[C_LOOKUPS] += (uint64_t)k;
+    cnt[C_HITS] += (uint64_t)nres;
+    cnt[C_MISSES] += (uint64_t)nmiss;
+    cnt[C_EVICT] += (uint64_t)nevict;
+    cnt[C_FILLED] += (uint64_t)nmiss * (uint64_t)a.sh.blob;
+    *a.L.ev_head = ev_head + (uint64_t)nmiss;
+#pragma unroll
+    for (int c = 0; c < C_N; ++c) a.L.counters[c] = cnt[c];
+    *a.L.step = t + 1;
+  }
+  span_end(a.span);
+}
+
 }  // namespace
 
 template <int NT>
@@ -613,6 +793,16 @@ static hipError_t launch_route_nt(int epl, const RouteArgs& a, hipStream_t st, K
   return sc_launch(k_route_remap<16, NT>, g, b, st, ev, a);
 }
 
+template <int SPL>
+static hipError_t launch_route_one_spl(int epl, const RouteArgs& a, hipStream_t st, KEvents ev) {
+  const dim3 g(1), b(64);
+  if (epl <= 1) return sc_launch(k_route_one<1, SPL>, g, b, st, ev, a);
+  if (epl <= 2) return sc_launch(k_route_one<2, SPL>, g, b, st, ev, a);
+  if (epl <= 4) return sc_launch(k_route_one<4, SPL>, g, b, st, ev, a);
+  if (epl <= 8) return sc_launch(k_route_one<8, SPL>, g, b, st, ev, a);
+  return sc_launch(k_route_one<16, SPL>, g, b, st, ev, a);
+}
+
 hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
                         const float* logits, int M, hipStream_t st, KEvents ev) {
   RouteArgs a;
@@ -623,6 +813,9 @@ hipError_t launch_route(const Shape& sh, const LayerDev& L, const Workspace& W,
   a.M = M;
   a.span = ev.span_for(1);
   const int epl = (sh.E + 63) / 64;
+  if (M == 1 && sh.k <= kRouteOneMaxK && sh.k <= L.S - L.P)
+    return L.S <= 128 ? launch_route_one_spl<2>(epl, a, st, ev)
+         : L.S <= 256 ? launch_route_one_spl<4>(epl, a, st, ev) : launch_route_one_spl<16>(epl, a, st, ev);
   if (M * sh.k >= kRouteWidePicks) return launch_route_nt<kRouteWideThreads>(epl, a, st, ev);
   return launch_route_nt<kRouteThreads>(epl, a, st, ev);
 }
