@@ -269,6 +269,181 @@ __device__ __forceinline__ float pick_weight(float zj, int k, int lane) {
   return ex / sum;
 }
 
+// Bookkeeping of a cached step of at most 64 picks on one wavefront, once its
+// rows are routed and the picks and the state snapshot are in LDS: pick p on
+// lane p, unique expert u on lane u.  The rules and every value written are
+// those of the block-wide passes of k_route_remap, without its block barriers.
+__device__ __forceinline__ void remap_small(const RouteArgs& a, int M, int P, const int* s_pick, int* s_first,
+                                         int* s_last, int* s_uidx, int* s_uexp, const int* s_e2s,
+                                         const int* s_s2e, const long long* s_key, uint8_t* s_ref, int64_t t,
+                                         uint64_t ev_head, uint64_t (&cnt)[C_N]) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.sh.E, k = a.sh.k, S = a.L.S, Pn = a.L.P;
+  const int64_t B = a.sh.blob;
+  const uint64_t below = (1ull << lane) - 1ull;
+
+  // unique experts in first-occurrence order (the LDS operations of one
+  // wavefront take effect in program order)
+  const bool act = lane < P;
+  const int e = act ? s_pick[lane] : 0;
+  if (act) {
+    atomicMin(&s_first[e], lane);
+    atomicMax(&s_last[e], lane);
+  }
+  const bool first = act && s_first[e] == lane;
+  const uint64_t fm = __ballot(first);
+  const int U = __popcll(fm);
+  if (first) {
+    const int r = __popcll(fm & below);
+    s_uexp[r] = e;
+    s_uidx[e] = r;
+  }
+
+  // residency against the slot map
+  const bool uact = lane < U;
+  const int ue = uact ? s_uexp[lane] : 0;
+  int sl = uact ? s_e2s[ue] : -1;
+  if (uact && (sl < -1 || sl >= S)) {
+    atomicOr(a.L.error, 1u);
+    sl = -1;
+  }
+  const bool miss = uact && sl < 0;
+  const uint64_t mm = __ballot(miss);
+  const int nmiss = __popcll(mm), mrank = __popcll(mm & below);
+  const int npin = __popcll(__ballot(uact && sl >= 0 && sl < Pn));
+  const bool bypass = U - npin > S - Pn;
+  const int nres = U - nmiss;
+  int nevict = 0;
+  if (!bypass) {
+    if (nmiss > 0) {
+      // victims: the nmiss least (key, slot) among unpinned slots not hit,
+      // one wavefront minimum per miss over packed (key + 2, slot)
+      for (int c = lane; c < S; c += 64) s_ref[c] = 0;
+      if (uact && sl >= 0) s_ref[sl] = 1;
+      constexpr int SPL = kMaxSlots / 64;
+      uint64_t ck[SPL];
+#pragma unroll
+      for (int q = 0; q < SPL; ++q) {
+        const int c = lane + 64 * q;
+        ck[q] = (c >= Pn && c < S && !s_ref[c]) ? (((uint64_t)(s_key[c] + 2) << 11) | (uint64_t)c) : ~0ull;
+      }
+      int my_victim = -1;
+      for (int i = 0; i < nmiss; ++i) {
+        uint64_t loc = ~0ull;
+#pragma unroll
+        for (int q = 0; q < SPL; ++q) loc = ck[q] < loc ? ck[q] : loc;
+        const uint64_t g = wave_reduce_u64<false>(loc);
+#pragma unroll
+        for (int q = 0; q < SPL; ++q)
+          if (ck[q] == g) ck[q] = ~0ull;
+        if (lane == i) my_victim = g == ~0ull ? -1 : (int)(g & 0x7FFull);
+      }
+      const int v = __shfl(my_victim, miss ? mrank : 0);
+      int old = -1;
+      if (miss) {
+        if (v < 0 || v >= S) {
+          // no victim (cannot happen while |U| <= S): read this expert from the
+          // backing store, leave the maps alone, and make the fill skip it
+          atomicOr(a.L.error, 4u);
+          a.W.miss_src[mrank] = nullptr;
+          a.W.miss_dst[mrank] = nullptr;
+        } else {
+          old = s_s2e[v];
+          if (old >= E) {
+            atomicOr(a.L.error, 2u);
+            old = -1;
+          }
+          if (old >= 0) a.L.e2s[old] = -1;
+          a.L.e2s[ue] = v;
+          a.L.s2e[v] = ue;
+          sl = v;
+          sc_event ev;
+          ev.step = t;
+          ev.expert = ue;
+          ev.slot = v;
+          ev.evicted = old;
+          ev.reserved = 0;
+          a.L.events[(ev_head + (uint64_t)mrank) % (uint64_t)a.L.ev_cap] = ev;
+          a.W.miss_src[mrank] = a.L.backing + (size_t)ue * B;
+          a.W.miss_dst[mrank] = a.L.slots + (size_t)v * B;
+        }
+      }
+      nevict = __popcll(__ballot(old >= 0));
+    }
+    // stamp the clock, publish slot pointers and the resident-first order
+    if (uact) {
+      a.W.uniq_order[miss ? nres + mrank : lane - mrank] = lane;
+      if (sl >= 0) {
+        a.L.key[sl] = t * (int64_t)(kCachedRows * k) + (int64_t)s_last[ue];
+        a.W.uniq_ptr[lane] = a.L.slots + (size_t)sl * B;
+      } else {
+        a.W.uniq_ptr[lane] = a.L.backing + (size_t)ue * B;
+      }
+    }
+  } else if (uact) {
+    // bypass: resident experts from their slots, the others read in place from the backing store
+    a.W.uniq_ptr[lane] = sl >= 0 ? a.L.slots + (size_t)sl * B : a.L.backing + (size_t)ue * B;
+    a.W.uniq_order[lane] = lane;
+  }
+  if (uact) a.W.uniq_expert[lane] = ue;
+
+  // picks grouped by unique expert (CSR), ascending pick order
+  if (U == P) {
+    if (act) {
+      a.W.pick_u[lane] = lane;
+      a.W.uniq_picks[lane] = lane;
+      a.W.uniq_off[lane] = lane;
+    }
+  } else {
+    const int up = act ? s_uidx[e] : -1;
+    int r = 0, c = 0;
+    for (int u = 0; u < U; ++u) {
+      const uint64_t m = __ballot(up == u);
+      if (up == u) r = __popcll(m & below);
+      if (lane == u) c = __popcll(m);
+    }
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const int ex = incl - c;
+    const int base = __shfl(ex, up >= 0 ? up : 0);
+    if (act) {
+      a.W.pick_u[lane] = up;
+      a.W.uniq_picks[base + r] = lane;
+    }
+    if (uact) a.W.uniq_off[lane] = ex;
+  }
+
+  if (lane == 0) {
+    a.W.uniq_off[U] = P;
+    a.W.hdr[H_UNIQUE] = U;
+    a.W.hdr[H_MISS] = bypass ? 0 : nmiss;
+    a.W.hdr[H_BYPASS] = bypass ? 1 : 0;
+    a.W.hdr[H_ROWS] = M;
+    a.W.hdr[H_RESIDENT] = U - nmiss;
+    a.W.hdr[H_STAGED] = 0;
+    cnt[C_STEPS] += 1;
+    if (bypass) {
+      cnt[C_BYPASS] += 1;
+      cnt[C_BYPASS_BYTES] += (uint64_t)nmiss * (uint64_t)B;
+    } else {
+      cnt[C_PICKS] += (uint64_t)P;
+      cnt[C_LOOKUPS] += (uint64_t)U;
+      cnt[C_HITS] += (uint64_t)(U - nmiss);
+      cnt[C_MISSES] += (uint64_t)nmiss;
+      cnt[C_EVICT] += (uint64_t)nevict;
+      cnt[C_FILLED] += (uint64_t)nmiss * (uint64_t)B;
+      *a.L.ev_head = ev_head + (uint64_t)nmiss;
+    }
+#pragma unroll
+    for (int c = 0; c < C_N; ++c) a.L.counters[c] = cnt[c];
+    *a.L.step = t + 1;
+  }
+}
+
 template <int EPL, int NT>
 __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
   constexpr int SPT = kMaxSlots / NT;   // slots per thread
@@ -288,18 +463,25 @@ __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
   __shared__ int s_wc[NT / 64];
   __shared__ unsigned long long s_wmin[NT / 64];
   __shared__ int s_nevict;
+  __shared__ long long s_t;
+  __shared__ unsigned long long s_evh;
 
   span_start(a.span);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.sh.E, k = a.sh.k, M = a.M, S = a.L.S;
   const int P = M * k;
-  const int64_t t = *a.L.step;
-  const uint64_t ev_head = *a.L.ev_head;
+  // The clock and the event head are read by one thread and passed on
+  // through LDS once the rows are routed: a uniform value loaded here would
+  // be moved to scalar registers at once, making every later load wait for it.
   uint64_t cnt[C_N];
+  int64_t t0 = 0;
+  uint64_t evh0 = 0;
   if (tid == 0) {
 #pragma unroll
     for (int c = 0; c < C_N; ++c) cnt[c] = a.L.counters[c];
+    t0 = *a.L.step;
+    evh0 = *a.L.ev_head;
   }
 
   // Layer state and the first logits rows are loaded up front; the state
@@ -359,8 +541,20 @@ __global__ __launch_bounds__(NT) void k_route_remap(RouteArgs a) {
       s_key[sl] = (long long)r_key[q];
     }
   }
-  if (tid == 0) s_nevict = 0;
+  if (tid == 0) {
+    s_nevict = 0;
+    s_t = t0;
+    s_evh = evh0;
+  }
   __syncthreads();
+  const int64_t t = s_t;
+  const uint64_t ev_head = s_evh;
+  if (P <= 64 && M <= kCachedRows) {
+    if (wave == 0) remap_small(a, M, P, s_pick, s_first, s_last, s_uidx, s_uexp, s_e2s, s_s2e, s_key, s_ref, t,
+                               ev_head, cnt);
+    span_end(a.span);
+    return;
+  }
 
   // ---- unique experts in first-occurrence order ----------------------------
   for (int p = tid; p < P; p += NT) {
