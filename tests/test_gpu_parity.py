@@ -700,6 +700,57 @@ def test_other_layer_shapes_against_the_oracle(shape):
     sc.close()
 
 
+# Layers aimed at the routing kernel's paths: one-row steps on one wavefront
+# (experts and slots over 64, 256 and 512, so several values per lane; up to
+# 16 picks; k equal to the unpinned slot count), the four-wavefront kernel on
+# a one-row step that can bypass, and steps of at most 64 picks (bookkeeping
+# on one wavefront, with bypasses) next to a step of 128 picks.
+ROUTE_CASES = {
+    "one_e300_k16_s200": dict(E=300, k=16, S=200, npin=5, Ms=[1] * 40),
+    "one_e1000_k16_s260": dict(E=1000, k=16, S=260, npin=0, Ms=[1] * 40),
+    "one_e100_k6_s50": dict(E=100, k=6, S=50, npin=0, Ms=[1] * 24),
+    "one_k_fills_unpinned": dict(E=300, k=12, S=16, npin=4, Ms=[1] * 16),
+    "one_row_may_bypass": dict(E=300, k=12, S=15, npin=4, Ms=[1] * 16),
+    "small_steps": dict(E=200, k=8, S=40, npin=3, Ms=[2, 3, 4, 8, 5, 1, 8, 7, 2, 6, 16, 4, 8, 3]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROUTE_CASES))
+def test_route_paths_against_the_oracle(case):
+    """Every step's ids, weights, events, slot map, keys and counters bit for
+    bit, and outputs to the tolerance, on layers that send steps down each
+    path of the routing kernel; the popular experts shift every few steps, so
+    the cached paths take misses, evictions and victim searches."""
+    p = ROUTE_CASES[case]
+    E, k, S, npin, Ms = p["E"], p["k"], p["S"], p["npin"], p["Ms"]
+    maxM = max(Ms)
+    log("route paths: %s (E=%d k=%d S=%d pins=%d M=%s)" % (case, E, k, S, npin, Ms))
+    cfg = WorkloadConfig("route_" + case, 256, 128, E, k, S, rows=maxM, steps=len(Ms), seed=91)
+    sc = make_cache(cfg, max_rows=maxM, gs_mode="uniform")
+    orc = _oracle_layer(cfg, S, "uniform")
+    rng = np.random.default_rng(37)
+    if npin:
+        pins = [int(e) for e in rng.permutation(E)[:npin]]
+        sc.pin(0, pins)
+        orc.state.pin(pins)
+    zs = []
+    for t in range(len(Ms)):
+        if t % 4 == 0:
+            hot = rng.permutation(E)[: max(k, E // 5)]
+        z = rng.standard_normal((maxM, E)).astype(np.float32)
+        z[:, hot] += 2.0
+        zs.append(z)
+    worst = _run_trace(cfg, sc, orc, len(Ms), lambda t: Ms[t], lambda t: zs[t])
+    st = sc.stats(0)
+    log("route paths %s: worst rel L2 %.3g, stats %s" % (case, worst, st))
+    assert st["misses"] > 0
+    if case == "one_row_may_bypass" or case == "small_steps":
+        assert st["bypass_steps"] > 0
+    else:
+        assert st["bypass_steps"] == 0 and st["evictions"] > 0
+    sc.close()
+
+
 def _random_layer(rng, i):
     """A small random layer: expert count, top-k, slots, pins, row mix, staging."""
     H, I = [(256, 128), (512, 256), (256, 256), (1024, 128)][i % 4]
