@@ -1631,7 +1631,10 @@ hipError_t launch_fill_gateup(const Shape& sh, const Workspace& W, const float* 
   FillGateupFn fn = pick_fill_gateup(sh.H);
   if (!fn) return hipErrorInvalidValue;
   GemvArgs a = gateup_args(sh, W, gs, x, -1);
-  const int blocks = one_row_gateup_blocks(sh);
+  // the product blocks fit beside the copy blocks (three blocks per compute
+  // unit at this kernel's registers), so none waits for the copy to end
+  int blocks = one_row_gateup_blocks(sh);
+  if (blocks > kGateupBlocks - kFillBlocksShared) blocks = kGateupBlocks - kFillBlocksShared;
   a.span = ev.span_for(blocks);
   FillArgs f;
   f.hdr = W.hdr;
