@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-drafted", action="store_true",
                     help="skip the drafted-rows workload (GLM layer, M = 4 / 16 / 64 schedule) in the default run")
     ap.add_argument("--no-link", action="store_true", help="skip the host-link DMA ceiling measurement")
+    ap.add_argument("--no-overlap-compare", action="store_true",
+                    help="skip the second pass of the churning workload with the overlapped miss fill "
+                         "(SC_FLAG_OVERLAP_FILL) in the default run")
     ap.add_argument("--banks", type=int, default=4, help="host backing banks of the stack workloads")
     ap.add_argument("--no-static", action="store_true", help="stack workloads: skip the static-pin comparator pass")
     ap.add_argument("--sweep-rows", default="",
@@ -1201,6 +1204,23 @@ def main():
         result["roofline_gemv_pair"] = dict(all_hit["gemv_pair"], down=all_hit["down"])
         result["all_hit"] = {k: v for k, v in all_hit.items() if k not in ("gateup", "down", "gemv_pair")}
     result["host_link"] = dict(fill, dma=link)
+    if not a.overlap_fill and not a.no_overlap_compare and a.config == "glm":
+        # the same steps from the same warmed state with the opt-in overlapped miss fill
+        print("bench: churning workload with the overlapped miss fill", file=sys.stderr, flush=True)
+        import copy
+        a_ov = copy.copy(a)
+        a_ov.overlap_fill = True
+        ov = churn_headline(a_ov, torch, env)
+        result["overlap_fill_workload"] = {
+            "flag": "SC_FLAG_OVERLAP_FILL",
+            "value": round(ov["value"], 3), "graph_reps_us": ov["reps_us"],
+            "vs_plain": round(ov["value"] / value, 4),
+            "hit_rate": ov["lru"]["hit_rate"], "misses": ov["lru"]["misses"],
+            "step_us_eager_all_hit_steps": ov["step_us_eager_all_hit_steps"],
+            "step_us_eager_miss_steps": ov["step_us_eager_miss_steps"],
+            "fill_GBs": ov["fill"]["achieved_GBs"],
+            "timing": "as value, same trace and warm-up, the misses copied while the resident experts' gate/up runs",
+        }
     # the pages' decode token model ("GLM 5.3 Testing: HBM Expert Allocation", section "What the physics says
     # to expect"): every token runs each of the 75 MoE layers once, plus about 3 ms of non-MoE work
     result["token_model"] = {"n_moe_layers": 75, "us_per_layer_step": round(value, 3), "other_ms": 3.0,
