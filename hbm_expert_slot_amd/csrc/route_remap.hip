@@ -269,10 +269,11 @@ __device__ __forceinline__ float pick_weight(float zj, int k, int lane) {
   return ex / sum;
 }
 
-// Bookkeeping of a cached step of at most 64 picks on one wavefront, once its
-// rows are routed and the picks and the state snapshot are in LDS: pick p on
-// lane p, unique expert u on lane u.  The rules and every value written are
-// those of the block-wide passes of k_route_remap, without its block barriers.
+// Bookkeeping of a step of at most 16 rows and 64 picks (cached, or a bypass
+// when its experts do not fit) on one wavefront, once its rows are routed and
+// the picks and the state snapshot are in LDS: pick p on lane p, unique
+// expert u on lane u.  The rules and every value written are those of the
+// block-wide passes of k_route_remap, without its block barriers.
 __device__ __forceinline__ void remap_small(const RouteArgs& a, int M, int P, const int* s_pick, int* s_first,
                                          int* s_last, int* s_uidx, int* s_uexp, const int* s_e2s,
                                          const int* s_s2e, const long long* s_key, uint8_t* s_ref, int64_t t,
