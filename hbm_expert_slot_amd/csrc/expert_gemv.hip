@@ -76,7 +76,12 @@ __device__ __forceinline__ int unique_at(const GemvArgs& a, int lo, int j) {
   return a.group < 0 ? j : a.order[lo + j];
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// SiLU from the hardware exponential and reciprocal (v_exp_f32 of -g log2(e),
+// v_rcp_f32: a few ulps in all, far inside the fp32 accumulation error of g
+// and u).  Below about g = -88 the exponential is +inf and the result -0.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
 
 // h as the matrix-core down product reads it: each group of 8 elements is 16
 // bytes of bf16 high parts then 16 bytes of bf16 low parts (hi = bf16(v), lo =
@@ -138,9 +143,24 @@ __device__ __forceinline__ void fp4x8_f32(uint32_t c, f32x2 (&w)[4]) {
   w[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
 }
 
-// Sum over one lane's 32 elements of one chunk: codes q (16 B), two block
-// scales in sc (bytes 0, 1), bf16 activation pairs xv[16].
-__device__ __forceinline__ float seg_dot_bf16(const uint4& q, uint32_t sc, const uint32_t* xv) {
+// The two E4M3 block scales in bytes 0 and 1 of sc, widened by one
+// instruction (the conversion is exact).
+__device__ __forceinline__ f32x2 scales2(uint32_t sc) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false); }
+
+// v_dot2_f32_bf16 with an inline zero accumulator: the builtin's form first
+// zeroes a register with a move.  Same operation and result.
+__device__ __forceinline__ float dot2_bf16_z(bf16x2 a, bf16x2 b) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// A row's running sum over its chunks: acc + b0 s0 + b1 s1, where b0 and b1
+// are one lane's sums over the two 16-element blocks of its 32 elements of one
+// chunk (codes q, 16 B; block scales in bytes 0 and 1 of sc; bf16 activation
+// pairs xv[16]).  A row's sum starts from -0, so the first chunk adds exactly
+// b0 s0 + b1 s1 rounded as the fused multiply-adds round it.
+__device__ __forceinline__ float seg_dot_bf16(const uint4& q, uint32_t sc, const uint32_t* xv, float acc_in) {
   const uint32_t d[4] = {q.x, q.y, q.z, q.w};
   float b[2];
 #pragma unroll
@@ -153,18 +173,18 @@ __device__ __forceinline__ float seg_dot_bf16(const uint4& q, uint32_t sc, const
 #pragma unroll
       for (int sel = 0; sel < 4; ++sel) {
         bf16x2 xx = __builtin_bit_cast(bf16x2, xv[(blk * 2 + dw) * 4 + sel]);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(w[sel], xx, acc, false);
+        acc = dw == 0 && sel == 0 ? dot2_bf16_z(w[sel], xx) : __builtin_amdgcn_fdot2_f32_bf16(w[sel], xx, acc, false);
       }
     }
     b[blk] = acc;
   }
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
-  return fmaf(b[1], s1, b[0] * s0);
+  const f32x2 sw = scales2(sc);
+  const float s0 = sw.x, s1 = sw.y;
+  return fmaf(b[1], s1, fmaf(b[0], s0, acc_in));
 }
 
 // Same with fp32 activations hv[32].
-__device__ __forceinline__ float seg_dot_f32(const uint4& q, uint32_t sc, const float* hv) {
+__device__ __forceinline__ float seg_dot_f32(const uint4& q, uint32_t sc, const float* hv, float acc_in) {
   const uint32_t d[4] = {q.x, q.y, q.z, q.w};
   float b[2];
 #pragma unroll
@@ -183,9 +203,9 @@ __device__ __forceinline__ float seg_dot_f32(const uint4& q, uint32_t sc, const 
     }
     b[blk] = acc;
   }
-  const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
-  const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
-  return fmaf(b[1], s1, b[0] * s0);
+  const f32x2 sw = scales2(sc);
+  const float s0 = sw.x, s1 = sw.y;
+  return fmaf(b[1], s1, fmaf(b[0], s0, acc_in));
 }
 
 // Sum NV values per lane over the LPR lanes of a row group with a transposed
@@ -304,7 +324,8 @@ struct Gemv {
   }
 
   // seg_dot_f32 with the codes already widened: w[4 * dw + sel] from dword dw
-  __device__ static __forceinline__ float blocks_dot_f32(const f32x2 (&w)[16], float s0, float s1, const float* hv) {
+  __device__ static __forceinline__ float blocks_dot_f32(const f32x2 (&w)[16], float s0, float s1, const float* hv,
+                                                        float acc_in) {
     float bsum[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -316,7 +337,7 @@ struct Gemv {
       }
       bsum[blk] = acc;
     }
-    return fmaf(bsum[1], s1, bsum[0] * s0);
+    return fmaf(bsum[1], s1, fmaf(bsum[0], s0, acc_in));
   }
 
   __device__ static __forceinline__ void process(const Buf& b, const uint32_t (&opw)[MR][NSEG][OPW],
@@ -327,7 +348,7 @@ struct Gemv {
       // down with several picks: each row's codes are widened once and serve
       // every pick (same products and order as seg_dot_f32)
 #pragma unroll
-      for (int e = 0; e < NV; ++e) v0[e] = 0.0f;
+      for (int e = 0; e < NV; ++e) v0[e] = -0.0f;
 #pragma unroll
       for (int j = 0; j < R; ++j) {
 #pragma unroll
@@ -341,12 +362,12 @@ struct Gemv {
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[4 * dw + e] = t[e];
           }
-          const float s0 = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
-          const float s1 = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
+          const f32x2 sw = scales2(b.sc[j][0][c]);
+          const float s0 = sw.x, s1 = sw.y;
 #pragma unroll
           for (int mi = 0; mi < MR; ++mi)
             if (mi < nc)
-              v0[j * MR + mi] += blocks_dot_f32(w, s0, s1, reinterpret_cast<const float*>(opw[mi][c]));
+              v0[j * MR + mi] = blocks_dot_f32(w, s0, s1, reinterpret_cast<const float*>(opw[mi][c]), v0[j * MR + mi]);
           // one row's widened codes live at a time
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -356,15 +377,15 @@ struct Gemv {
     for (int j = 0; j < R; ++j) {
 #pragma unroll
       for (int mi = 0; mi < MR; ++mi) {
-        float acc0 = 0.0f, acc1 = 0.0f;
+        float acc0 = -0.0f, acc1 = -0.0f;
         if (mi < nc) {
 #pragma unroll
           for (int c = 0; c < NSEG; ++c) {
             if (GATEUP) {
-              acc0 += seg_dot_bf16(b.q[j][0][c], b.sc[j][0][c], opw[mi][c]);
-              acc1 += seg_dot_bf16(b.q[j][NM - 1][c], b.sc[j][NM - 1][c], opw[mi][c]);
+              acc0 = seg_dot_bf16(b.q[j][0][c], b.sc[j][0][c], opw[mi][c], acc0);
+              acc1 = seg_dot_bf16(b.q[j][NM - 1][c], b.sc[j][NM - 1][c], opw[mi][c], acc1);
             } else {
-              acc0 += seg_dot_f32(b.q[j][0][c], b.sc[j][0][c], reinterpret_cast<const float*>(opw[mi][c]));
+              acc0 = seg_dot_f32(b.q[j][0][c], b.sc[j][0][c], reinterpret_cast<const float*>(opw[mi][c]), acc0);
             }
           }
         }
@@ -372,6 +393,19 @@ struct Gemv {
         v1[j * MR + mi] = acc1;
       }
     }
+    }
+    if constexpr (GATEUP && NV == 1 && LPR == 64) {
+      // one row over the whole wavefront: its gate and up sums are reduced
+      // together (each by the same tree as alone), lanes 0-31 ending with the
+      // gate sum and lanes 32-63 with the up sum
+      float gu[2] = {v0[0], v1[0]};
+      XRed<32, 2>::run(gu, lane);
+      const float gsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gu[0]), 0));
+      const float usum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gu[0]), 32));
+      if (lane == 0 && nc > 0 && i < n)
+        store_h(a.out + (size_t)pk[0] * a.rows, base + i * stride, silu_f32(gsum * gs) * (usum * gs),
+                !SINGLE && a.split_h);
+      return;
     }
     XRed<LPR / 2, NV>::run(v0, lane);
     if (GATEUP) XRed<LPR / 2, NV>::run(v1, lane);
@@ -551,17 +585,20 @@ struct GemvShared {
   }
 
   // seg_dot_bf16 with the codes already widened: w[4 * dw + sel] from dword dw
-  __device__ static __forceinline__ float blocks_dot(const bf16x2 (&w)[16], float s0, float s1, const uint32_t* xv) {
+  __device__ static __forceinline__ float blocks_dot(const bf16x2 (&w)[16], float s0, float s1, const uint32_t* xv,
+                                                     float acc_in) {
     float bsum[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       float acc = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(w[blk * 8 + e], __builtin_bit_cast(bf16x2, xv[blk * 8 + e]), acc, false);
+      for (int e = 0; e < 8; ++e) {
+        const bf16x2 xx = __builtin_bit_cast(bf16x2, xv[blk * 8 + e]);
+        acc = e == 0 ? dot2_bf16_z(w[blk * 8 + e], xx) : __builtin_amdgcn_fdot2_f32_bf16(w[blk * 8 + e], xx, acc, false);
+      }
       bsum[blk] = acc;
     }
-    return fmaf(bsum[1], s1, bsum[0] * s0);
+    return fmaf(bsum[1], s1, fmaf(bsum[0], s0, acc_in));
   }
 
   __device__ static __forceinline__ void process(const Buf& b, const uint8_t* lds, const int (&pk)[MRX], int nc, int i,
@@ -570,8 +607,8 @@ struct GemvShared {
     float v0[NV], v1[NV];
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
-      v0[e] = 0.0f;
-      v1[e] = 0.0f;
+      v0[e] = -0.0f;
+      v1[e] = -0.0f;
     }
     if constexpr (GATEUP) {
       // each chunk's codes are widened once, then used by every pick
@@ -593,10 +630,11 @@ struct GemvShared {
 #pragma unroll
             for (int e = 0; e < 4; ++e) wu[j][4 * dw + e] = t[e];
           }
-          sg[j][0] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
-          sg[j][1] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
-          su[j][0] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][1][c], 0);
-          su[j][1] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][1][c], 1);
+          const f32x2 g2 = scales2(b.sc[j][0][c]), u2 = scales2(b.sc[j][1][c]);
+          sg[j][0] = g2.x;
+          sg[j][1] = g2.y;
+          su[j][0] = u2.x;
+          su[j][1] = u2.y;
         }
 #pragma unroll
         for (int m = 0; m < MRX; ++m) {
@@ -605,8 +643,8 @@ struct GemvShared {
             xread(lds, m, c, seg, xv);
 #pragma unroll
             for (int j = 0; j < R; ++j) {
-              v0[j * MRX + m] += blocks_dot(wg[j], sg[j][0], sg[j][1], xv);
-              v1[j * MRX + m] += blocks_dot(wu[j], su[j][0], su[j][1], xv);
+              v0[j * MRX + m] = blocks_dot(wg[j], sg[j][0], sg[j][1], xv, v0[j * MRX + m]);
+              v1[j * MRX + m] = blocks_dot(wu[j], su[j][0], su[j][1], xv, v1[j * MRX + m]);
             }
           }
         }
@@ -628,8 +666,9 @@ struct GemvShared {
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[j][4 * dw + e] = t[e];
           }
-          s0[j] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 0);
-          s1[j] = __builtin_amdgcn_cvt_f32_fp8(b.sc[j][0][c], 1);
+          const f32x2 sw = scales2(b.sc[j][0][c]);
+          s0[j] = sw.x;
+          s1[j] = sw.y;
         }
 #pragma unroll
         for (int m = 0; m < MRX; ++m) {
@@ -638,8 +677,9 @@ struct GemvShared {
             xread(lds, m, c, seg, xv);
 #pragma unroll
             for (int j = 0; j < R; ++j)
-              v0[j * MRX + m] += Gemv<K, 1, R, false>::blocks_dot_f32(w[j], s0[j], s1[j],
-                                                                     reinterpret_cast<const float*>(xv));
+              v0[j * MRX + m] = Gemv<K, 1, R, false>::blocks_dot_f32(w[j], s0[j], s1[j],
+                                                                    reinterpret_cast<const float*>(xv),
+                                                                    v0[j * MRX + m]);
           }
         }
       }
@@ -885,8 +925,8 @@ struct GemvMfmaL {
         const int slot = (4 * ktp + g) ^ (j % PPR);
         const uint4 q4 = *reinterpret_cast<const uint4*>(buf + j * (KC / 2) + 16 * slot);
         const uint32_t sc = *reinterpret_cast<const uint16_t*>(buf + CODE_B + j * (KC / 16) + 8 * ktp + 2 * g);
-        const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
-        const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
+        const f32x2 sw = scales2(sc);
+        const float s0 = sw.x, s1 = sw.y;
         const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1127,8 +1167,8 @@ struct GemvMfmaX {
         const int slot = (4 * ktp + g) ^ (j % PPR);
         const uint4 q4 = *reinterpret_cast<const uint4*>(buf + j * (KC / 2) + 16 * slot);
         const uint32_t sc = *reinterpret_cast<const uint16_t*>(buf + CODE_B + j * (KC / 16) + 8 * ktp + 2 * g);
-        const float s0 = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
-        const float s1 = __builtin_amdgcn_cvt_f32_fp8(sc, 1);
+        const f32x2 sw = scales2(sc);
+        const float s0 = sw.x, s1 = sw.y;
         const uint32_t d[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
