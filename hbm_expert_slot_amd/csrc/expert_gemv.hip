@@ -340,9 +340,11 @@ struct Gemv {
     return fmaf(bsum[1], s1, fmaf(bsum[0], s0, acc_in));
   }
 
+  // hq: the one-row gate/up's pending sums (see below); unused otherwise
   __device__ static __forceinline__ void process(const Buf& b, const uint32_t (&opw)[MR][NSEG][OPW],
                                                  const int (&pk)[MR], int nc, int i, int n, int base,
-                                                 int stride, int lane, int rsub, float gs, const GemvArgs& a) {
+                                                 int stride, int lane, int rsub, float gs, const GemvArgs& a,
+                                                 float& hq) {
     float v0[NV], v1[NV];
     if constexpr (!GATEUP && MR > 1) {
       // down with several picks: each row's codes are widened once and serve
@@ -400,11 +402,19 @@ struct Gemv {
       // gate sum and lanes 32-63 with the up sum
       float gu[2] = {v0[0], v1[0]};
       XRed<32, 2>::run(gu, lane);
-      const float gsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gu[0]), 0));
-      const float usum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gu[0]), 32));
-      if (lane == 0 && nc > 0 && i < n)
-        store_h(a.out + (size_t)pk[0] * a.rows, base + i * stride, silu_f32(gsum * gs) * (usum * gs),
-                !SINGLE && a.split_h);
+      // Row step i's gate sum waits in lane i % 32 of hq and its up sum in
+      // lane 32 + i % 32; every 32 row steps, and after the run's last, lanes
+      // 0-31 take SiLU(gate) * up of the row steps they hold and store them
+      // together (the rows are consecutive).
+      const int t = i & 31;
+      hq = (lane & 31) == t ? gu[0] : hq;
+      if (t == 31 || i + 1 >= n) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(hq), __float_as_uint(hq), false, false);
+        const float g = __uint_as_float(sw[0]), u = __uint_as_float(sw[1]);   // lanes 0-31: own and lane + 32
+        if (lane <= t && nc > 0)
+          store_h(a.out + (size_t)pk[0] * a.rows, base + (i - t + lane) * stride, silu_f32(g * gs) * (u * gs),
+                  !SINGLE && a.split_h);
+      }
       return;
     }
     XRed<LPR / 2, NV>::run(v0, lane);
@@ -503,14 +513,15 @@ struct Gemv {
             }
           }
         }
+        float hq = 0.0f;
         int i = 0;
         while (true) {
           if (i + R < n) load(B, code_base, scale_base, i + R, n, base, stride, rsub, a.up_row0);
-          process(A, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a);
+          process(A, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a, hq);
           i += R;
           if (i >= n) break;
           if (i + R < n) load(A, code_base, scale_base, i + R, n, base, stride, rsub, a.up_row0);
-          process(B, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a);
+          process(B, opw, pk, nc, i, n, base, stride, lane, rsub, gs, a, hq);
           i += R;
           if (i >= n) break;
         }
