@@ -417,6 +417,16 @@ struct Gemv {
       }
       return;
     }
+    if constexpr (!GATEUP && MR == 1) {
+      // a lane holds the sum of row step i + j, j = (lane % LPR) / (LPR / NV):
+      // one store for the stage's R rows
+      XRed<LPR / 2, NV>::run(v0, lane);
+      const int g = lane % LPR;
+      const int j = g / (LPR / NV);
+      if (g % (LPR / NV) == 0 && nc > 0 && i + j < n)
+        a.out[(size_t)pk[0] * a.rows + (base + (i + j) * stride) * RPW + rsub] = v0[0] * gs;
+      return;
+    }
     XRed<LPR / 2, NV>::run(v0, lane);
     if (GATEUP) XRed<LPR / 2, NV>::run(v1, lane);
     const int g = lane % LPR;
