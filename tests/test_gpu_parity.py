@@ -677,6 +677,26 @@ OTHER_SHAPES = {"h512_i256": (512, 256), "h1024_i512": (1024, 512), "h2048_i1024
 
 
 @pytest.mark.timeout(600)
+def test_one_row_runs_longer_than_32_row_steps():
+    """A one-row step whose gate/up wavefronts each compute more than 32 row
+    steps (H 2048, I 4096, 32 picks: 42 or 43 per wavefront), so the kernel
+    writes the SiLU outputs of a run in more than one batch: bookkeeping bit
+    for bit and every output against the oracle."""
+    H, I, E, k, S = 2048, 4096, 32, 32, 32
+    cfg = WorkloadConfig("long_runs", H, I, E, k, S, rows=1, steps=3, seed=67)
+    log("long runs: H=%d I=%d E=%d k=%d S=%d, 3 one-row steps" % (H, I, E, k, S))
+    sc = make_cache(cfg, max_rows=1, gs_mode="uniform")
+    orc = _oracle_layer(cfg, S, "uniform")
+    rng = np.random.default_rng(71)
+    zs = [rng.standard_normal((1, E)).astype(np.float32) for _ in range(3)]
+    worst = _run_trace(cfg, sc, orc, 3, lambda t: 1, lambda t: zs[t])
+    st = sc.stats(0)
+    log("long runs: worst rel L2 %.3g, stats %s" % (worst, st))
+    assert st["misses"] == E and st["hits"] == 2 * E
+    sc.close()
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("shape", list(OTHER_SHAPES))
 def test_other_layer_shapes_against_the_oracle(shape):
     """One-row, two-row (streaming), matrix-core and bypass steps on layer
